@@ -1,0 +1,238 @@
+"""Seeded synthetic inputs for exact attention and its KV-cache decode variant.
+
+This module only draws random tensors and builds the rotary cos/sin tables that
+callers pass in as inputs.  It holds none of the attention arithmetic, so both
+the fp64 oracle and the HIP path can consume what it produces without sharing
+any method code.
+
+Conventions (the pages' test scripts draw with ``torch.rand`` / ``torch.randn``
+and seed with ``torch.random.manual_seed(0)``; flash-attention PR #99
+"Added Support for Rotary Positional Embeddings", test parametrisation diff):
+
+* one CPU ``torch.Generator`` per workload, seeded, draws in the listed order;
+* integer draws (``cache_seqlens``) first, then floating draws in fp32,
+  converted to the working dtype with round-to-nearest-even (``.to(dtype)``);
+* tensors use the flash layout ``[batch, seqlen, heads, head_dim]`` (the
+  skill page "Flash Attention - Fast Memory-Efficient Attention", Workflow 2
+  Step 2), except the empty-cache workload, which draws in
+  ``[batch, heads, seqlen, dim]`` and hands over ``.transpose(1, 2)`` views
+  exactly like the first script of flash-attention issue #1402;
+* rotary tables are ``[seqlen_ro, rotary_dim // 2]``: the angle of position p
+  and pair j is ``p * base ** (-2j / rotary_dim)``, evaluated in fp64, then cos
+  and sin are rounded to the working dtype (issue #1402, second script; PR #99,
+  rotary kernel argument review).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+def rope_tables(seqlen_ro: int, rotary_dim: int, base: float, dtype: torch.dtype):
+    """cos/sin tables ``[seqlen_ro, rotary_dim // 2]`` in ``dtype`` (inputs, not results)."""
+    assert rotary_dim % 2 == 0
+    j = np.arange(rotary_dim // 2, dtype=np.float64)
+    inv_freq = base ** (-2.0 * j / rotary_dim)
+    pos = np.arange(seqlen_ro, dtype=np.float64)
+    ang = np.outer(pos, inv_freq)
+    cos = torch.from_numpy(np.cos(ang)).to(dtype)
+    sin = torch.from_numpy(np.sin(ang)).to(dtype)
+    return cos.contiguous(), sin.contiguous()
+
+
+@dataclass
+class FwdCase:
+    """Inputs for ``attn_fwd``: q [B,Sq,Hq,Dqk], k [B,Sk,Hkv,Dqk], v [B,Sk,Hkv,Dv]."""
+    name: str
+    dtype: str
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    causal: bool
+    softmax_scale: float | None
+
+
+@dataclass
+class KVCacheCase:
+    """Inputs for ``attn_fwd_kvcache``.
+
+    q [B,Sq,Hq,Dqk]; k_cache [B,cap,Hkv,Dqk]; v_cache [B,cap,Hkv,Dv];
+    k_new/v_new [B,Snew,Hkv,D*] or None; cache_seqlens an int or an int32 [B]
+    tensor; rotary_cos/sin [seqlen_ro, rd/2] or None.
+    """
+    name: str
+    dtype: str
+    q: torch.Tensor
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    k_new: torch.Tensor | None
+    v_new: torch.Tensor | None
+    cache_seqlens: object
+    rotary_cos: torch.Tensor | None = None
+    rotary_sin: torch.Tensor | None = None
+    rotary_interleaved: bool = False
+    causal: bool = False
+    softmax_scale: float | None = None
+    extra: dict = field(default_factory=dict)
+
+
+def _randn(g, shape, dtype):
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(DTYPES[dtype])
+
+
+def _rand(g, shape, dtype):
+    return torch.rand(shape, generator=g, dtype=torch.float32).to(DTYPES[dtype])
+
+
+# ---------------------------------------------------------------------------
+# The five workloads
+# ---------------------------------------------------------------------------
+
+def kvcache_empty(seed: int = 0) -> KVCacheCase:
+    """Empty cache, B=4, H=16, D=16, Sq=Snew=2, fp16, k=v=q (aliased views).
+
+    Mirrors the first script of flash-attention issue #1402: a uniform[0,1)
+    query reused as key and value, a zero cache of the same shape, the
+    integer ``cache_seqlens=0``, non-causal, default scale 1/sqrt(16).
+    """
+    g = torch.Generator().manual_seed(seed)
+    q_bhsd = _rand(g, (4, 16, 2, 16), "fp16")
+    kc = torch.zeros_like(q_bhsd)
+    vc = torch.zeros_like(q_bhsd)
+    q = q_bhsd.transpose(1, 2)
+    return KVCacheCase("kvcache_empty_b4h16d16", "fp16", q=q,
+                       k_cache=kc.transpose(1, 2), v_cache=vc.transpose(1, 2),
+                       k_new=q, v_new=q, cache_seqlens=0, causal=False,
+                       softmax_scale=None)
+
+
+def fwd_d64(causal: bool, seed: int = 0) -> FwdCase:
+    """attn_fwd B=2, H=8, S=2048, D=64, fp16, N(0,1), scale 1/8."""
+    g = torch.Generator().manual_seed(seed)
+    q = _randn(g, (2, 2048, 8, 64), "fp16")
+    k = _randn(g, (2, 2048, 8, 64), "fp16")
+    v = _randn(g, (2, 2048, 8, 64), "fp16")
+    return FwdCase("fwd_b2h8s2048d64" + ("_causal" if causal else ""), "fp16",
+                   q, k, v, causal, 1.0 / 8.0)
+
+
+def decode_gqa(seed: int = 0, capacity: int = 8192) -> KVCacheCase:
+    """Decode step: B=8, Hq=32, Hkv=8, D=128, bf16, cap 8192, Snew=1, RoPE rd=128 non-interleaved."""
+    g = torch.Generator().manual_seed(seed)
+    seqlens = torch.randint(1, 8000, (8,), generator=g, dtype=torch.int32)
+    q = _randn(g, (8, 1, 32, 128), "bf16")
+    k_new = _randn(g, (8, 1, 8, 128), "bf16")
+    v_new = _randn(g, (8, 1, 8, 128), "bf16")
+    k_cache = _randn(g, (8, capacity, 8, 128), "bf16")
+    v_cache = _randn(g, (8, capacity, 8, 128), "bf16")
+    cos, sin = rope_tables(capacity, 128, 10000.0, torch.bfloat16)
+    return KVCacheCase("decode_gqa_b8hq32hkv8d128", "bf16", q=q, k_cache=k_cache,
+                       v_cache=v_cache, k_new=k_new, v_new=v_new,
+                       cache_seqlens=seqlens, rotary_cos=cos, rotary_sin=sin,
+                       rotary_interleaved=False, causal=True,
+                       softmax_scale=1.0 / math.sqrt(128))
+
+
+def chunked_prefill(seed: int = 0, capacity: int = 4096, snew: int = 512) -> KVCacheCase:
+    """Chunked prefill: B=4, H=16, D=128, bf16, cap 4096, 512 new tokens, RoPE rd=64 interleaved, causal."""
+    g = torch.Generator().manual_seed(seed)
+    seqlens = torch.randint(0, 2048, (4,), generator=g, dtype=torch.int32)
+    q = _randn(g, (4, snew, 16, 128), "bf16")
+    k_new = _randn(g, (4, snew, 16, 128), "bf16")
+    v_new = _randn(g, (4, snew, 16, 128), "bf16")
+    k_cache = _randn(g, (4, capacity, 16, 128), "bf16")
+    v_cache = _randn(g, (4, capacity, 16, 128), "bf16")
+    cos, sin = rope_tables(capacity, 64, 10000.0, torch.bfloat16)
+    return KVCacheCase("chunked_prefill_b4h16d128", "bf16", q=q, k_cache=k_cache,
+                       v_cache=v_cache, k_new=k_new, v_new=v_new,
+                       cache_seqlens=seqlens, rotary_cos=cos, rotary_sin=sin,
+                       rotary_interleaved=True, causal=True,
+                       softmax_scale=1.0 / math.sqrt(128))
+
+
+def fwd_asym(seed: int = 0, S: int = 4096) -> FwdCase:
+    """attn_fwd causal B=2, H=16, S=4096, Dqk=192, Dv=128, bf16, scale 1/sqrt(192)."""
+    g = torch.Generator().manual_seed(seed)
+    q = _randn(g, (2, S, 16, 192), "bf16")
+    k = _randn(g, (2, S, 16, 192), "bf16")
+    v = _randn(g, (2, S, 16, 128), "bf16")
+    return FwdCase("fwd_asym_b2h16s%dd192v128" % S, "bf16", q, k, v, True,
+                   1.0 / math.sqrt(192))
+
+
+# ---------------------------------------------------------------------------
+# Generic random cases (parity tests at oracle-friendly sizes)
+# ---------------------------------------------------------------------------
+
+def random_fwd(B, Sq, Sk, Hq, Hkv, Dqk, Dv, dtype, causal, seed=0,
+               softmax_scale=None, dist="randn") -> FwdCase:
+    g = torch.Generator().manual_seed(seed)
+    draw = _randn if dist == "randn" else _rand
+    q = draw(g, (B, Sq, Hq, Dqk), dtype)
+    k = draw(g, (B, Sk, Hkv, Dqk), dtype)
+    v = draw(g, (B, Sk, Hkv, Dv), dtype)
+    return FwdCase("random_fwd", dtype, q, k, v, causal, softmax_scale)
+
+
+def random_kvcache(B, Sq, Hq, Hkv, Dqk, Dv, capacity, dtype, *, snew, seqlens,
+                   rotary_dim=0, interleaved=False, causal=True, seed=0,
+                   softmax_scale=None, seqlens_as_tensor=True,
+                   tail_fill=None) -> KVCacheCase:
+    """Random kvcache case.  ``seqlens`` is an int or a list of B ints.
+
+    ``tail_fill`` (e.g. ``float('nan')``) overwrites every cache row at or
+    beyond ``cache_seqlens[b] + snew`` so stray reads show up in the output.
+    """
+    g = torch.Generator().manual_seed(seed)
+    q = _randn(g, (B, Sq, Hq, Dqk), dtype)
+    k_new = _randn(g, (B, snew, Hkv, Dqk), dtype) if snew else None
+    v_new = _randn(g, (B, snew, Hkv, Dv), dtype) if snew else None
+    k_cache = _randn(g, (B, capacity, Hkv, Dqk), dtype)
+    v_cache = _randn(g, (B, capacity, Hkv, Dv), dtype)
+    lens = [seqlens] * B if isinstance(seqlens, int) else list(seqlens)
+    if tail_fill is not None:
+        for b in range(B):
+            k_cache[b, lens[b] + snew:] = tail_fill
+            v_cache[b, lens[b] + snew:] = tail_fill
+    cos = sin = None
+    if rotary_dim:
+        cos, sin = rope_tables(capacity, rotary_dim, 10000.0, DTYPES[dtype])
+    cs = torch.tensor(lens, dtype=torch.int32) if seqlens_as_tensor else int(lens[0])
+    return KVCacheCase("random_kvcache", dtype, q=q, k_cache=k_cache, v_cache=v_cache,
+                       k_new=k_new, v_new=v_new, cache_seqlens=cs,
+                       rotary_cos=cos, rotary_sin=sin, rotary_interleaved=interleaved,
+                       causal=causal, softmax_scale=softmax_scale)
+
+
+def seqlens_list(cs, B):
+    """cache_seqlens (int or tensor) as a list of B Python ints."""
+    if isinstance(cs, torch.Tensor):
+        return [int(x) for x in cs.tolist()]
+    return [int(cs)] * B
+
+
+# Algorithmic work per workload (what the method must do, independent of tiling).
+
+def fwd_flops(B, Sq, Sk, Hq, Dqk, Dv, causal):
+    """2*(Dqk+Dv) flop per unmasked (query, key) pair; causal keeps key <= query (+Sk-Sq)."""
+    if causal:
+        pairs = sum(max(0, min(Sk, i + 1 + Sk - Sq)) for i in range(Sq))
+    else:
+        pairs = Sq * Sk
+    return 2.0 * (Dqk + Dv) * B * Hq * pairs
+
+
+def kvcache_pairs(lens, Sq, snew, causal):
+    tot = 0
+    for c in lens:
+        L = c + snew
+        if causal:
+            tot += sum(min(L, c + i + 1) for i in range(Sq))
+        else:
+            tot += Sq * L
+    return tot
