@@ -1,0 +1,274 @@
+"""Python binding of libattn (exact attention for MI355X / gfx950).
+
+Argument marshalling only: torch tensors are turned into device pointers,
+element strides and the current HIP stream, and handed to the C ABI declared
+in include/attn.h.  Every step of the computation runs in the library's HIP
+kernels; there is no fallback.  If libattn.so is missing, importing this
+package raises ImportError (build it with ``python -m
+exact_attention_qk_amd.build`` or ``__graft_entry__.build()``).
+
+Names follow the pages: ``attn_fwd`` (flash_attn_func), ``attn_fwd_kvcache``
+(flash_attn_with_kvcache) and ``rope_apply`` (the non-fused rotary kernel).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # loads the HIP runtime the library must share (load order matters)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libattn.so not found at %s: build it first "
+                      "(python -m exact_attention_qk_amd.build)" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+ATTN_OK = 0
+ERRORS = {-1: "ATTN_E_NULL", -2: "ATTN_E_SHAPE", -3: "ATTN_E_UNSUPPORTED", -4: "ATTN_E_ALIGN",
+          -5: "ATTN_E_WORKSPACE", -6: "ATTN_E_OVERFLOW", -7: "ATTN_E_HIP"}
+EXPORTED = ["attn_fwd", "attn_fwd_kvcache", "attn_fwd_kvcache_workspace_size", "rope_apply",
+            "attn_validate_fwd", "attn_validate_kvcache", "attn_validate_rope",
+            "attn_last_error", "attn_abi_version"]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("%s (%d): %s" % (ERRORS.get(code, "?"), code, msg))
+        self.code = code
+
+
+class Tensor4(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_s", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+
+
+class FwdParams(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("B", ctypes.c_int), ("Sq", ctypes.c_int),
+                ("Sk", ctypes.c_int), ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int),
+                ("Dqk", ctypes.c_int), ("Dv", ctypes.c_int),
+                ("q", Tensor4), ("k", Tensor4), ("v", Tensor4), ("out", Tensor4),
+                ("lse", ctypes.c_void_p), ("causal", ctypes.c_int),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class KVCacheParams(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("B", ctypes.c_int), ("Sq", ctypes.c_int),
+                ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int), ("Dqk", ctypes.c_int),
+                ("Dv", ctypes.c_int), ("capacity", ctypes.c_int), ("Snew", ctypes.c_int),
+                ("q", Tensor4), ("k_cache", Tensor4), ("v_cache", Tensor4),
+                ("k_new", Tensor4), ("v_new", Tensor4), ("out", Tensor4),
+                ("cache_seqlens_scalar", ctypes.c_int), ("cache_seqlens", ctypes.c_void_p),
+                ("rotary_cos", ctypes.c_void_p), ("rotary_sin", ctypes.c_void_p),
+                ("rotary_dim", ctypes.c_int), ("seqlen_ro", ctypes.c_int),
+                ("rotary_interleaved", ctypes.c_int), ("causal", ctypes.c_int),
+                ("softmax_scale", ctypes.c_float), ("lse", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("num_splits", ctypes.c_int)]
+
+
+class RopeParams(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("B", ctypes.c_int), ("S", ctypes.c_int),
+                ("H", ctypes.c_int), ("D", ctypes.c_int), ("x", Tensor4), ("out", Tensor4),
+                ("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p),
+                ("rotary_dim", ctypes.c_int), ("seqlen_ro", ctypes.c_int),
+                ("interleaved", ctypes.c_int), ("conjugate", ctypes.c_int),
+                ("offset_scalar", ctypes.c_int), ("offsets", ctypes.c_void_p)]
+
+
+_lib.attn_fwd.argtypes = [ctypes.POINTER(FwdParams), ctypes.c_void_p]
+_lib.attn_fwd_kvcache.argtypes = [ctypes.POINTER(KVCacheParams), ctypes.c_void_p]
+_lib.attn_fwd_kvcache_workspace_size.argtypes = [ctypes.POINTER(KVCacheParams)]
+_lib.attn_fwd_kvcache_workspace_size.restype = ctypes.c_size_t
+_lib.rope_apply.argtypes = [ctypes.POINTER(RopeParams), ctypes.c_void_p]
+_lib.attn_validate_fwd.argtypes = [ctypes.POINTER(FwdParams)]
+_lib.attn_validate_kvcache.argtypes = [ctypes.POINTER(KVCacheParams)]
+_lib.attn_validate_rope.argtypes = [ctypes.POINTER(RopeParams)]
+_lib.attn_last_error.restype = ctypes.c_char_p
+for _n in ("attn_fwd", "attn_fwd_kvcache", "rope_apply", "attn_validate_fwd",
+           "attn_validate_kvcache", "attn_validate_rope", "attn_abi_version"):
+    getattr(_lib, _n).restype = ctypes.c_int
+
+_DT = {torch.float16: 0, torch.bfloat16: 1}
+
+
+def lib():
+    return _lib
+
+
+def _check(code):
+    if code != ATTN_OK:
+        raise AttnError(code, _lib.attn_last_error().decode())
+
+
+def _t4(t):
+    if t is None:
+        return Tensor4(None, 0, 0, 0)
+    assert t.dim() == 4, "expected a [batch, seqlen, heads, head_dim] tensor"
+    if t.shape[-1] > 1:
+        assert t.stride(-1) == 1, "head_dim must be contiguous"
+    return Tensor4(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _dtype(t):
+    if t.dtype not in _DT:
+        raise AttnError(-3, "dtype %s is not float16 or bfloat16" % t.dtype)
+    return _DT[t.dtype]
+
+
+def _scale(s):
+    return float("nan") if s is None else float(s)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream) if t.is_cuda else None
+
+
+# ---------------------------------------------------------------- attn_fwd
+
+def fwd_params(q, k, v, out, causal=False, softmax_scale=None, lse=None):
+    B, Sq, Hq, Dqk = q.shape
+    Sk, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    return FwdParams(_dtype(q), B, Sq, Sk, Hq, Hkv, Dqk, Dv, _t4(q), _t4(k), _t4(v), _t4(out),
+                     lse.data_ptr() if lse is not None else None, int(bool(causal)),
+                     _scale(softmax_scale))
+
+
+def attn_fwd(q, k, v, causal=False, softmax_scale=None, out=None, return_lse=False):
+    """Exact attention.  q [B,Sq,Hq,Dqk], k [B,Sk,Hkv,Dqk], v [B,Sk,Hkv,Dv] -> out [B,Sq,Hq,Dv]."""
+    B, Sq, Hq, _ = q.shape
+    Dv = v.shape[3]
+    if out is None:
+        out = torch.empty((B, Sq, Hq, Dv), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
+    p = fwd_params(q, k, v, out, causal, softmax_scale, lse)
+    _check(_lib.attn_fwd(ctypes.byref(p), _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+# ---------------------------------------------------------------- kvcache
+
+def kvcache_params(q, k_cache, v_cache, k=None, v=None, rotary_cos=None, rotary_sin=None,
+                   cache_seqlens=0, causal=False, softmax_scale=None, rotary_interleaved=False,
+                   out=None, lse=None, workspace=None, num_splits=0):
+    B, Sq, Hq, Dqk = q.shape
+    cap, Hkv, Dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    snew = 0 if k is None else k.shape[1]
+    if isinstance(cache_seqlens, torch.Tensor):
+        assert cache_seqlens.dtype == torch.int32 and cache_seqlens.is_contiguous()
+        cs_scalar, cs_ptr = 0, cache_seqlens.data_ptr()
+    else:
+        cs_scalar, cs_ptr = int(cache_seqlens), None
+    rd = seq_ro = 0
+    if rotary_cos is not None:
+        seq_ro, rd = rotary_cos.shape[0], 2 * rotary_cos.shape[1]
+    return KVCacheParams(
+        _dtype(q), B, Sq, Hq, Hkv, Dqk, Dv, cap, snew,
+        _t4(q), _t4(k_cache), _t4(v_cache), _t4(k), _t4(v), _t4(out),
+        cs_scalar, cs_ptr,
+        rotary_cos.data_ptr() if rotary_cos is not None else None,
+        rotary_sin.data_ptr() if rotary_sin is not None else None,
+        rd, seq_ro, int(bool(rotary_interleaved)), int(bool(causal)), _scale(softmax_scale),
+        lse.data_ptr() if lse is not None else None,
+        workspace.data_ptr() if workspace is not None and workspace.numel() else None,
+        workspace.numel() if workspace is not None else 0, int(num_splits))
+
+
+def kvcache_workspace_size(params: KVCacheParams) -> int:
+    return int(_lib.attn_fwd_kvcache_workspace_size(ctypes.byref(params)))
+
+
+def attn_fwd_kvcache(q, k_cache, v_cache, k=None, v=None, rotary_cos=None, rotary_sin=None,
+                     cache_seqlens=0, causal=False, softmax_scale=None, rotary_interleaved=None,
+                     num_splits=0, out=None, return_lse=False, workspace=None):
+    """flash_attn_with_kvcache: append k/v at cache_seqlens (in place), then attend.
+
+    ``rotary_interleaved`` must be given whenever rotary tables are passed.
+    """
+    if rotary_cos is not None and rotary_interleaved is None:
+        raise ValueError("rotary_interleaved must be given explicitly with rotary tables")
+    B, Sq, Hq, _ = q.shape
+    Dv = v_cache.shape[3]
+    if out is None:
+        out = torch.empty((B, Sq, Hq, Dv), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
+    p = kvcache_params(q, k_cache, v_cache, k, v, rotary_cos, rotary_sin, cache_seqlens, causal,
+                       softmax_scale, bool(rotary_interleaved), out, lse, None, num_splits)
+    need = kvcache_workspace_size(p)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+    off = (-workspace.data_ptr()) % 256
+    ws = workspace[off:]
+    p.workspace = ws.data_ptr() if need else None
+    p.workspace_bytes = ws.numel()
+    _check(_lib.attn_fwd_kvcache(ctypes.byref(p), _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+# ---------------------------------------------------------------- rope
+
+def rope_params(x, cos, sin, offsets=0, interleaved=False, conjugate=False, out=None):
+    B, S, H, D = x.shape
+    if isinstance(offsets, torch.Tensor):
+        off_s, off_p = 0, offsets.data_ptr()
+    else:
+        off_s, off_p = int(offsets), None
+    return RopeParams(_dtype(x), B, S, H, D, _t4(x), _t4(out if out is not None else x),
+                      cos.data_ptr(), sin.data_ptr(), 2 * cos.shape[1], cos.shape[0],
+                      int(bool(interleaved)), int(bool(conjugate)), off_s, off_p)
+
+
+def rope_apply(x, cos, sin, offsets=0, interleaved=False, conjugate=False, out=None, inplace=False):
+    """Rotate the first 2*cos.shape[1] dims of x [B,S,H,D] at positions offsets + s."""
+    if out is None:
+        out = x if inplace else torch.empty_like(x)
+    p = rope_params(x, cos, sin, offsets, interleaved, conjugate, out)
+    _check(_lib.rope_apply(ctypes.byref(p), _stream(x)))
+    return out
+
+
+# ---------------------------------------------------------------- prepared calls
+
+class PreparedCall:
+    """A C-ABI call whose parameter block is built once (for timing loops and graphs).
+
+    The tensors referenced by the parameters must stay alive and in place for as
+    long as the prepared call is used.
+    """
+
+    def __init__(self, fn, params, stream, keep):
+        self._fn, self._p, self._stream, self._keep = fn, params, stream, keep
+        self._ref = ctypes.byref(params)
+
+    def __call__(self):
+        code = self._fn(self._ref, self._stream)
+        if code != ATTN_OK:
+            _check(code)
+
+
+def prepare_fwd(q, k, v, out, causal=False, softmax_scale=None, lse=None):
+    p = fwd_params(q, k, v, out, causal, softmax_scale, lse)
+    return PreparedCall(_lib.attn_fwd, p, _stream(q), (q, k, v, out, lse))
+
+
+def prepare_kvcache(q, k_cache, v_cache, k, v, out, *, rotary_cos=None, rotary_sin=None,
+                    cache_seqlens=0, causal=False, softmax_scale=None, rotary_interleaved=False,
+                    num_splits=0, lse=None):
+    p = kvcache_params(q, k_cache, v_cache, k, v, rotary_cos, rotary_sin, cache_seqlens, causal,
+                       softmax_scale, rotary_interleaved, out, lse, None, num_splits)
+    need = kvcache_workspace_size(p)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+    off = (-ws.data_ptr()) % 256
+    p.workspace = ws.data_ptr() + off if need else None
+    p.workspace_bytes = need
+    return PreparedCall(_lib.attn_fwd_kvcache, p, _stream(q),
+                        (q, k_cache, v_cache, k, v, out, rotary_cos, rotary_sin, cache_seqlens,
+                         lse, ws))
+
+
+__all__ = ["PreparedCall", "prepare_fwd", "prepare_kvcache", "attn_fwd", "attn_fwd_kvcache", "rope_apply", "kvcache_workspace_size", "AttnError",
+           "FwdParams", "KVCacheParams", "RopeParams", "Tensor4", "fwd_params", "kvcache_params",
+           "rope_params", "lib", "EXPORTED", "LIB_PATH"]

@@ -1,0 +1,392 @@
+// C ABI of libattn: argument validation, workspace planning and kernel
+// dispatch.  Everything here is host code; it never allocates device memory
+// and never reads device memory unless ATTN_CHECK=1 asks it to validate the
+// device-side cache lengths.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "attn.h"
+#include "launchers.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return ATTN_OK;
+}
+
+bool dims_supported(int dqk, int dv) {
+  return (dqk == 16 && dv == 16) || (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) ||
+         (dqk == 192 && dv == 128);
+}
+
+int check_dtype(attn_dtype d) {
+  if (d != ATTN_DTYPE_F16 && d != ATTN_DTYPE_BF16)
+    return fail(ATTN_E_UNSUPPORTED, "dtype %d is not fp16 (0) or bf16 (1)", (int)d);
+  return ATTN_OK;
+}
+
+int check_tensor(const attn_tensor4& t, const char* name) {
+  if (!t.data) return fail(ATTN_E_NULL, "%s: data pointer is NULL", name);
+  if (reinterpret_cast<uintptr_t>(t.data) % 16)
+    return fail(ATTN_E_ALIGN, "%s: data pointer is not 16-byte aligned", name);
+  if (t.stride_b % 8 || t.stride_s % 8 || t.stride_h % 8)
+    return fail(ATTN_E_ALIGN, "%s: strides (%lld, %lld, %lld) must be multiples of 8 elements", name,
+                (long long)t.stride_b, (long long)t.stride_s, (long long)t.stride_h);
+  if (t.stride_b < 0 || t.stride_s < 0 || t.stride_h < 0)
+    return fail(ATTN_E_SHAPE, "%s: negative stride", name);
+  return ATTN_OK;
+}
+
+float resolve_c(float scale, int dqk) {
+  const float s = std::isnan(scale) ? 1.0f / std::sqrt((float)dqk) : scale;
+  return s * 1.4426950408889634f;
+}
+
+attn::AttnArgs base_args() {
+  attn::AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  return a;
+}
+
+void set_q(attn::AttnArgs& a, const attn_tensor4& t) {
+  a.q = static_cast<const uint16_t*>(t.data); a.q_sb = t.stride_b; a.q_ss = t.stride_s; a.q_sh = t.stride_h;
+}
+void set_k(attn::AttnArgs& a, const attn_tensor4& t) {
+  a.k = static_cast<const uint16_t*>(t.data); a.k_sb = t.stride_b; a.k_ss = t.stride_s; a.k_sh = t.stride_h;
+}
+void set_v(attn::AttnArgs& a, const attn_tensor4& t) {
+  a.v = static_cast<const uint16_t*>(t.data); a.v_sb = t.stride_b; a.v_ss = t.stride_s; a.v_sh = t.stride_h;
+}
+void set_o(attn::AttnArgs& a, const attn_tensor4& t) {
+  a.out = static_cast<uint16_t*>(t.data); a.o_sb = t.stride_b; a.o_ss = t.stride_s; a.o_sh = t.stride_h;
+}
+
+// ---------------------------------------------------------------- kvcache plan
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct KVPlan {
+  bool rotary = false;
+  bool decode = false;      // split-KV path (few query rows per kv head)
+  int split_len = 0, num_splits = 0;
+  size_t off_qrot = 0, off_o = 0, off_ml = 0, total = 0;
+};
+
+KVPlan plan_kvcache(const attn_kvcache_params* p) {
+  KVPlan k;
+  k.rotary = p->rotary_cos != nullptr;
+  const int group = p->Hq / p->Hkv;
+  const int R = group * p->Sq;
+  k.decode = R <= 16;
+  size_t off = 0;
+  if (k.rotary) {
+    k.off_qrot = off;
+    off = align_up(off + (size_t)p->B * p->Sq * p->Hq * p->Dqk * 2);
+  }
+  if (k.decode) {
+    const int cap = p->capacity;
+    int len;
+    if (p->num_splits > 0) {
+      len = (cap + p->num_splits - 1) / p->num_splits;
+    } else {
+      const double per = (double)cap * p->B * p->Hkv / 4096.0;
+      len = (int)std::ceil(per);
+      if (len > 2048) len = 2048;
+    }
+    len = (len + 31) / 32 * 32;
+    if (len < 32) len = 32;
+    k.split_len = len;
+    k.num_splits = (cap + len - 1) / len;
+    const size_t slots = (size_t)p->B * p->Hkv * k.num_splits * R;
+    k.off_o = off;
+    off = align_up(off + slots * p->Dv * sizeof(float));
+    k.off_ml = off;
+    off = align_up(off + slots * 2 * sizeof(float));
+  }
+  k.total = off;
+  return k;
+}
+
+int validate_fwd(const attn_fwd_params* p) {
+  if (!p) return fail(ATTN_E_NULL, "params pointer is NULL");
+  int e;
+  if ((e = check_dtype(p->dtype))) return e;
+  if (p->B < 0 || p->Sq < 0 || p->Sk < 0 || p->Hq < 1 || p->Hkv < 1)
+    return fail(ATTN_E_SHAPE, "sizes must satisfy B, Sq, Sk >= 0 and Hq, Hkv >= 1");
+  if (p->Hq % p->Hkv)
+    return fail(ATTN_E_SHAPE, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+  if (!dims_supported(p->Dqk, p->Dv))
+    return fail(ATTN_E_UNSUPPORTED, "(Dqk, Dv) = (%d, %d) is not one of (16,16), (64,64), (128,128), (192,128)",
+                p->Dqk, p->Dv);
+  if (p->B == 0 || p->Sq == 0) return ok();
+  if ((e = check_tensor(p->q, "q"))) return e;
+  if (p->Sk > 0) {
+    if ((e = check_tensor(p->k, "k"))) return e;
+    if ((e = check_tensor(p->v, "v"))) return e;
+  }
+  if ((e = check_tensor(p->out, "out"))) return e;
+  return ok();
+}
+
+int validate_kvcache(const attn_kvcache_params* p) {
+  if (!p) return fail(ATTN_E_NULL, "params pointer is NULL");
+  int e;
+  if ((e = check_dtype(p->dtype))) return e;
+  if (p->B < 0 || p->Sq < 0 || p->Hq < 1 || p->Hkv < 1 || p->capacity < 1 || p->Snew < 0)
+    return fail(ATTN_E_SHAPE, "sizes must satisfy B, Sq, Snew >= 0 and Hq, Hkv, capacity >= 1");
+  if (p->Hq % p->Hkv)
+    return fail(ATTN_E_SHAPE, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+  if (!dims_supported(p->Dqk, p->Dv))
+    return fail(ATTN_E_UNSUPPORTED, "(Dqk, Dv) = (%d, %d) is not one of (16,16), (64,64), (128,128), (192,128)",
+                p->Dqk, p->Dv);
+  if (p->Snew != 0 && p->Snew != p->Sq)
+    return fail(ATTN_E_SHAPE, "Snew (%d) must be 0 or equal to Sq (%d)", p->Snew, p->Sq);
+  if (p->Snew > p->capacity)
+    return fail(ATTN_E_OVERFLOW, "Snew (%d) exceeds the cache capacity (%d)", p->Snew, p->capacity);
+  if (!p->cache_seqlens) {
+    if (p->cache_seqlens_scalar < 0)
+      return fail(ATTN_E_SHAPE, "cache_seqlens (%d) is negative", p->cache_seqlens_scalar);
+    if ((int64_t)p->cache_seqlens_scalar + p->Snew > p->capacity)
+      return fail(ATTN_E_OVERFLOW, "cache_seqlens (%d) + Snew (%d) exceeds the capacity (%d)",
+                  p->cache_seqlens_scalar, p->Snew, p->capacity);
+  }
+  const bool rot = p->rotary_cos || p->rotary_sin;
+  if (rot) {
+    if (!p->rotary_cos || !p->rotary_sin)
+      return fail(ATTN_E_NULL, "rotary_cos and rotary_sin must both be given or both be NULL");
+    if (p->rotary_dim < 2 || p->rotary_dim % 2 || p->rotary_dim > p->Dqk)
+      return fail(ATTN_E_SHAPE, "rotary_dim (%d) must be even and in [2, Dqk=%d]", p->rotary_dim, p->Dqk);
+    if (p->seqlen_ro < 1) return fail(ATTN_E_SHAPE, "seqlen_ro must be >= 1");
+    if (!p->cache_seqlens &&
+        (int64_t)p->cache_seqlens_scalar + (p->Sq > p->Snew ? p->Sq : p->Snew) > p->seqlen_ro)
+      return fail(ATTN_E_SHAPE, "positions up to %d exceed the rotary tables (%d rows)",
+                  p->cache_seqlens_scalar + (p->Sq > p->Snew ? p->Sq : p->Snew) - 1, p->seqlen_ro);
+  }
+  if (p->num_splits < 0) return fail(ATTN_E_SHAPE, "num_splits must be >= 0");
+  if (p->B == 0 || p->Sq == 0) return ok();
+  if ((e = check_tensor(p->q, "q"))) return e;
+  if ((e = check_tensor(p->k_cache, "k_cache"))) return e;
+  if ((e = check_tensor(p->v_cache, "v_cache"))) return e;
+  if ((e = check_tensor(p->out, "out"))) return e;
+  if (p->Snew > 0) {
+    if ((e = check_tensor(p->k_new, "k_new"))) return e;
+    if ((e = check_tensor(p->v_new, "v_new"))) return e;
+  }
+  const KVPlan plan = plan_kvcache(p);
+  if (plan.total > 0) {
+    if (!p->workspace)
+      return fail(ATTN_E_WORKSPACE, "workspace of %zu bytes required, got NULL", plan.total);
+    if (p->workspace_bytes < plan.total)
+      return fail(ATTN_E_WORKSPACE, "workspace of %zu bytes required, got %zu", plan.total,
+                  p->workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(p->workspace) % kAlign)
+      return fail(ATTN_E_ALIGN, "workspace must be 256-byte aligned");
+  }
+  return ok();
+}
+
+int validate_rope(const attn_rope_params* p) {
+  if (!p) return fail(ATTN_E_NULL, "params pointer is NULL");
+  int e;
+  if ((e = check_dtype(p->dtype))) return e;
+  if (p->B < 0 || p->S < 0 || p->H < 0 || p->D < 8 || p->D % 8)
+    return fail(ATTN_E_SHAPE, "sizes must satisfy B, S, H >= 0 and D a positive multiple of 8");
+  if (p->rotary_dim < 0 || p->rotary_dim % 2 || p->rotary_dim > p->D)
+    return fail(ATTN_E_SHAPE, "rotary_dim (%d) must be even and in [0, D=%d]", p->rotary_dim, p->D);
+  if (p->seqlen_ro < 1) return fail(ATTN_E_SHAPE, "seqlen_ro must be >= 1");
+  if (!p->offsets) {
+    if (p->offset_scalar < 0) return fail(ATTN_E_SHAPE, "offset (%d) is negative", p->offset_scalar);
+    if ((int64_t)p->offset_scalar + p->S > p->seqlen_ro)
+      return fail(ATTN_E_SHAPE, "positions up to %d exceed the rotary tables (%d rows)",
+                  p->offset_scalar + p->S - 1, p->seqlen_ro);
+  }
+  if ((int64_t)p->B * p->S * p->H == 0) return ok();
+  if (p->rotary_dim > 0 && (!p->cos || !p->sin)) return fail(ATTN_E_NULL, "cos/sin table is NULL");
+  if ((e = check_tensor(p->x, "x"))) return e;
+  if ((e = check_tensor(p->out, "out"))) return e;
+  return ok();
+}
+
+bool env_check() {
+  const char* s = std::getenv("ATTN_CHECK");
+  return s && s[0] == '1';
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(ATTN_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return 1; }
+
+const char* attn_last_error(void) { return g_err.c_str(); }
+
+int attn_validate_fwd(const attn_fwd_params* p) { return validate_fwd(p); }
+int attn_validate_kvcache(const attn_kvcache_params* p) { return validate_kvcache(p); }
+int attn_validate_rope(const attn_rope_params* p) { return validate_rope(p); }
+
+int attn_fwd(const attn_fwd_params* p, void* stream) {
+  int e = validate_fwd(p);
+  if (e) return e;
+  if (p->B == 0 || p->Sq == 0) return ok();
+  attn::AttnArgs a = base_args();
+  set_q(a, p->q); set_k(a, p->k); set_v(a, p->v); set_o(a, p->out);
+  a.lse = p->lse;
+  a.B = p->B; a.Sq = p->Sq; a.Sk = p->Sk; a.Hq = p->Hq; a.Hkv = p->Hkv; a.group = p->Hq / p->Hkv;
+  a.kvcache = 0;
+  a.causal = p->causal ? 1 : 0;
+  a.c = resolve_c(p->softmax_scale, p->Dqk);
+  hipError_t he = attn::run_tile_attn(a, p->dtype == ATTN_DTYPE_BF16, p->Dqk, p->Dv, p->causal != 0,
+                                      static_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "attn_fwd launch");
+  return ok();
+}
+
+size_t attn_fwd_kvcache_workspace_size(const attn_kvcache_params* p) {
+  if (!p || p->Hkv < 1 || p->Hq < 1 || p->capacity < 1 || p->Hq % p->Hkv) return 0;
+  return plan_kvcache(p).total;
+}
+
+int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream) {
+  int e = validate_kvcache(p);
+  if (e) return e;
+  if (p->B == 0 || p->Sq == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const KVPlan plan = plan_kvcache(p);
+  const bool bf16 = p->dtype == ATTN_DTYPE_BF16;
+  const int maxrows = p->Sq > p->Snew ? p->Sq : p->Snew;
+
+  if (p->cache_seqlens && env_check()) {
+    std::vector<int32_t> h(p->B);
+    hipError_t he = hipMemcpyAsync(h.data(), p->cache_seqlens, sizeof(int32_t) * p->B,
+                                   hipMemcpyDeviceToHost, st);
+    if (he == hipSuccess) he = hipStreamSynchronize(st);
+    if (he != hipSuccess) return hip_fail(he, "ATTN_CHECK copy of cache_seqlens");
+    for (int b = 0; b < p->B; ++b) {
+      if (h[b] < 0 || (int64_t)h[b] + p->Snew > p->capacity)
+        return fail(ATTN_E_OVERFLOW, "cache_seqlens[%d] = %d with Snew %d does not fit capacity %d", b,
+                    h[b], p->Snew, p->capacity);
+      if (plan.rotary && (int64_t)h[b] + maxrows > p->seqlen_ro)
+        return fail(ATTN_E_SHAPE, "cache_seqlens[%d] = %d: positions exceed the rotary tables (%d rows)",
+                    b, h[b], p->seqlen_ro);
+    }
+  }
+
+  char* ws = static_cast<char*>(p->workspace);
+  uint16_t* qrot = plan.rotary ? reinterpret_cast<uint16_t*>(ws + plan.off_qrot) : nullptr;
+  const int64_t qr_sh = p->Dqk, qr_ss = (int64_t)p->Hq * p->Dqk, qr_sb = (int64_t)p->Sq * qr_ss;
+
+  // 1. append new rows (rotating keys) and rotate the queries
+  attn::RowSet sets[3];
+  int ns = 0;
+  auto rowset = [&](const attn_tensor4& x, const uint16_t* ydata, int64_t ysb, int64_t yss,
+                    int64_t ysh, int S, int H, int D, bool rotate, bool at_offset) {
+    attn::RowSet r;
+    std::memset(&r, 0, sizeof(r));
+    r.t.x = static_cast<const uint16_t*>(x.data);
+    r.t.x_sb = x.stride_b; r.t.x_ss = x.stride_s; r.t.x_sh = x.stride_h;
+    r.t.y = const_cast<uint16_t*>(ydata);
+    r.t.y_sb = ysb; r.t.y_ss = yss; r.t.y_sh = ysh;
+    r.t.B = p->B; r.t.S = S; r.t.H = H; r.t.D = D;
+    r.t.cos = static_cast<const uint16_t*>(p->rotary_cos);
+    r.t.sin = static_cast<const uint16_t*>(p->rotary_sin);
+    r.t.rd = rotate ? p->rotary_dim : 0;
+    r.t.interleaved = p->rotary_interleaved ? 1 : 0;
+    r.t.conjugate = 0;
+    r.t.offsets = p->cache_seqlens;
+    r.t.offset_scalar = p->cache_seqlens_scalar;
+    r.t.copy_only = rotate ? 0 : 1;
+    r.dst_at_offset = at_offset ? 1 : 0;
+    sets[ns++] = r;
+  };
+  if (p->Snew > 0) {
+    rowset(p->k_new, static_cast<uint16_t*>(p->k_cache.data), p->k_cache.stride_b, p->k_cache.stride_s,
+           p->k_cache.stride_h, p->Snew, p->Hkv, p->Dqk, plan.rotary, true);
+    rowset(p->v_new, static_cast<uint16_t*>(p->v_cache.data), p->v_cache.stride_b, p->v_cache.stride_s,
+           p->v_cache.stride_h, p->Snew, p->Hkv, p->Dv, false, true);
+  }
+  if (plan.rotary) rowset(p->q, qrot, qr_sb, qr_ss, qr_sh, p->Sq, p->Hq, p->Dqk, true, false);
+  if (ns > 0) {
+    hipError_t he = attn::run_rope_rows(sets, ns, bf16, st);
+    if (he != hipSuccess) return hip_fail(he, "kvcache append launch");
+  }
+
+  // 2. attention over the cache prefix
+  attn::AttnArgs a = base_args();
+  if (plan.rotary) {
+    a.q = qrot; a.q_sb = qr_sb; a.q_ss = qr_ss; a.q_sh = qr_sh;
+  } else {
+    set_q(a, p->q);
+  }
+  set_k(a, p->k_cache); set_v(a, p->v_cache); set_o(a, p->out);
+  a.lse = p->lse;
+  a.seqlens = p->cache_seqlens;
+  a.seqlen_scalar = p->cache_seqlens_scalar;
+  a.B = p->B; a.Sq = p->Sq; a.Sk = p->capacity; a.Hq = p->Hq; a.Hkv = p->Hkv; a.group = p->Hq / p->Hkv;
+  a.Snew = p->Snew;
+  a.kvcache = 1;
+  a.causal = p->causal ? 1 : 0;
+  a.c = resolve_c(p->softmax_scale, p->Dqk);
+  hipError_t he;
+  if (plan.decode) {
+    a.split_len = plan.split_len;
+    a.num_splits = plan.num_splits;
+    a.ws_o = reinterpret_cast<float*>(ws + plan.off_o);
+    a.ws_ml = reinterpret_cast<float*>(ws + plan.off_ml);
+    he = attn::run_decode_attn(a, bf16, p->Dqk, p->Dv, p->causal != 0, st);
+  } else {
+    he = attn::run_tile_attn(a, bf16, p->Dqk, p->Dv, p->causal != 0, st);
+  }
+  if (he != hipSuccess) return hip_fail(he, "kvcache attention launch");
+  return ok();
+}
+
+int rope_apply(const attn_rope_params* p, void* stream) {
+  int e = validate_rope(p);
+  if (e) return e;
+  if ((int64_t)p->B * p->S * p->H == 0) return ok();
+  attn::RowSet r;
+  std::memset(&r, 0, sizeof(r));
+  r.t.x = static_cast<const uint16_t*>(p->x.data);
+  r.t.x_sb = p->x.stride_b; r.t.x_ss = p->x.stride_s; r.t.x_sh = p->x.stride_h;
+  r.t.y = static_cast<uint16_t*>(p->out.data);
+  r.t.y_sb = p->out.stride_b; r.t.y_ss = p->out.stride_s; r.t.y_sh = p->out.stride_h;
+  r.t.B = p->B; r.t.S = p->S; r.t.H = p->H; r.t.D = p->D;
+  r.t.cos = static_cast<const uint16_t*>(p->cos);
+  r.t.sin = static_cast<const uint16_t*>(p->sin);
+  r.t.rd = p->rotary_dim;
+  r.t.interleaved = p->interleaved ? 1 : 0;
+  r.t.conjugate = p->conjugate ? 1 : 0;
+  r.t.offsets = p->offsets;
+  r.t.offset_scalar = p->offset_scalar;
+  r.t.copy_only = p->rotary_dim == 0 ? 1 : 0;
+  r.dst_at_offset = 0;
+  hipError_t he = attn::run_rope_rows(&r, 1, p->dtype == ATTN_DTYPE_BF16, static_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "rope_apply launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Kernel argument block shared by the attention kernels and the host dispatcher.
+#pragma once
+#include <stdint.h>
+
+namespace attn {
+
+struct AttnArgs {
+  const uint16_t* q;  int64_t q_sb, q_ss, q_sh;
+  const uint16_t* k;  int64_t k_sb, k_ss, k_sh;
+  const uint16_t* v;  int64_t v_sb, v_ss, v_sh;
+  uint16_t* out;      int64_t o_sb, o_ss, o_sh;
+  float* lse;                 // [B, Hq, Sq] or null
+  const int32_t* seqlens;     // per-batch cache_seqlens (kvcache mode) or null
+  int seqlen_scalar;          // cache_seqlens for every batch when seqlens is null
+  int B, Sq, Sk, Hq, Hkv, group, Snew;
+  int kvcache;                // 1: key length c_b + Snew, query i at c_b + i
+                              // 0: key length Sk, query i at i + Sk - Sq
+  int causal;                 // key j allowed for query i iff j <= position(i)
+  int num_qtiles;             // tiled kernel: ceil(Sq / rows per workgroup)
+  int xcd_remap;              // tiled kernel: 1 when the grid is a multiple of 8
+  float c;                    // softmax_scale * log2(e)
+  // split-KV decode
+  int split_len, num_splits;
+  float* ws_o;                // [B, Hkv, num_splits, R, Dv] fp32 partial numerators
+  float* ws_ml;               // [B, Hkv, num_splits, R, 2]  running max (log2 units), sum
+};
+
+struct RopeArgs {
+  const uint16_t* x;  int64_t x_sb, x_ss, x_sh;
+  uint16_t* y;        int64_t y_sb, y_ss, y_sh;
+  int B, S, H, D;
+  const uint16_t* cos; const uint16_t* sin;
+  int rd, interleaved, conjugate;
+  const int32_t* offsets; int offset_scalar;
+  int copy_only;              // 1: plain row copy (v rows of the cache append)
+};
+
+struct RowSet {
+  RopeArgs t;
+  int dst_at_offset;          // 1: destination row index = off_b + s, else s
+};
+
+}  // namespace attn

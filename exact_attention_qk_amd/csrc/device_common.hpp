@@ -1,0 +1,133 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+//
+// Layout facts used throughout (checked on gfx950 with a one-wave probe):
+//  * v_mfma_f32_32x32x16_{f16,bf16}: lane l holds A[l%32][8*(l/32)+j] and
+//    B[8*(l/32)+j][l%32] (j = 0..7); result element r of lane l is
+//    C[(r/4)*8 + 4*(l/32) + r%4][l%32].
+//  * v_mfma_f32_16x16x32_{f16,bf16}: lane l holds A[l%16][8*(l/16)+j] and
+//    B[8*(l/16)+j][l%16]; result element r of lane l is C[4*(l/16)+r][l%16].
+//  * ds_read_b64_tr_b16: inside each group of 16 lanes, output lane i gets
+//    element t (t = 0..3) from element i%4 of the 8 bytes read by input lane
+//    4t + i/4.  So if input lane 4t+q reads row t, columns c0+4q..c0+4q+3 of a
+//    row-major tile, output lane i holds column c0+i of rows 0..3: a transposed
+//    read that turns a row-major V tile into the MFMA operand that contracts
+//    over V's rows.
+//  * v_permlane32_swap(x, x) returns {x[l or l-32], x[l+32 or l]}; the max
+//    (or sum) of the two results combines lane l with lane l^32.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+// Element type traits: storage is always 16-bit; T selects MFMA flavour and conversions.
+struct F16 {
+  typedef _Float16 scalar;
+  typedef f16x8 vec8;
+  static __device__ __forceinline__ float to_f32(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+  }
+  static __device__ __forceinline__ uint16_t from_f32(float x) {  // round to nearest even
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    f16x2 v = __builtin_convertvector((f32x2){a, b}, f16x2);
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+
+struct BF16 {
+  typedef __bf16 scalar;
+  typedef bf16x8 vec8;
+  static __device__ __forceinline__ float to_f32(uint16_t b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+  }
+  static __device__ __forceinline__ uint16_t from_f32(float x) {  // round to nearest even
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    bf16x2 v = __builtin_convertvector((f32x2){a, b}, bf16x2);
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void stg16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// 8-byte transposed LDS read (see header comment).
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* lds_ptr) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(lds_ptr));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// max / sum of a value held by lane l and lane l^32.
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-byte chunk swizzles of row-major LDS tiles.  A tile row of D 16-bit
+// elements holds C = D/8 chunks; chunk c of row r is stored at position
+// c ^ swz(r) of that row.
+//  * K tiles are read 16 B per lane from 16 different rows at one chunk
+//    column; the swizzle spreads those 16 reads over all 64 banks.
+//  * V tiles are read by ds_read_b64_tr_b16: 4 consecutive rows x 2 adjacent
+//    chunks per 16-lane group; the swizzle puts the 4 row pairs on 4 disjoint
+//    bank ranges.
+template <int C>
+__device__ __forceinline__ int swz_k(int r) {
+  if constexpr (C % 16 == 0) return r & 15;
+  else if constexpr (C % 8 == 0) return (r >> 1) & 7;
+  else if constexpr (C == 4) return (r >> 2) & 3;
+  else if constexpr (C == 2) return (r >> 3) & 1;
+  else return 0;
+}
+template <int C>
+__device__ __forceinline__ int swz_v(int r) {
+  if constexpr (C % 16 == 0) return (r & 7) << 1;
+  else if constexpr (C % 8 == 0) return ((r >> 1) & 3) << 1;
+  else return 0;
+}
+
+}  // namespace attn

@@ -1,0 +1,12 @@
+// Host-side entry points of the kernel translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include "attn_args.hpp"
+
+namespace attn {
+hipError_t run_tile_attn(const AttnArgs& a, int dtype_bf16, int dqk, int dv, bool causal,
+                         hipStream_t st);
+hipError_t run_decode_attn(const AttnArgs& a, int dtype_bf16, int dqk, int dv, bool causal,
+                           hipStream_t st);
+hipError_t run_rope_rows(const RowSet* sets, int nsets, int dtype_bf16, hipStream_t st);
+}  // namespace attn

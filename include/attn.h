@@ -1,0 +1,200 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) exact-attention library (libattn.so).
+ *
+ * Three operations, named after the functions the pages discuss:
+ *
+ *   attn_fwd          exact attention softmax(scale * Q K^T + mask) V computed
+ *                     tile by tile with an online softmax, so the score matrix
+ *                     never reaches HBM.  The plain definition is the "standard
+ *                     attention" of the skill page "Flash Attention - Fast
+ *                     Memory-Efficient Attention" (Workflow 1, Step 2); the
+ *                     flash_attn_func call of that page (Quick start; Workflow 2
+ *                     Step 2) fixes the [batch, seqlen, heads, head_dim] layout,
+ *                     the causal flag, the automatic scale and (Workflow 2 Step 3)
+ *                     fewer K/V heads than q heads.  head_dim of q/k may differ
+ *                     from head_dim of v (flash-attention PR #1604 "Support
+ *                     hdimQK != hdimV backward", PR body: d=192 with d_v=128).
+ *
+ *   attn_fwd_kvcache  the decode-time variant flash_attn_with_kvcache
+ *                     (flash-attention issue #1402 "is flash_attn_with_kvcache()
+ *                     supposed to work for seqlen > 1 ?", both scripts): append
+ *                     k_new/v_new into a preallocated cache at per-batch
+ *                     cache_seqlens (an int for all batches or an int32 tensor
+ *                     with one value per batch: ROCm/flash-attention PR #99
+ *                     "Added Support for Rotary Positional Embeddings (both
+ *                     non-fused and fused kernel)", rotary kernel argument
+ *                     review), optionally rotating q and k_new (RoPE) with
+ *                     cos/sin tables offset by the cache position, then attend
+ *                     q over the cache prefix.
+ *
+ *   rope_apply        the same rotation as a standalone (non-fused) operation
+ *                     (PR #99 title: fused and non-fused rotary), with the
+ *                     conjugate (inverse-angle) flag named in that PR's review.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are described by attn_tensor4: a device pointer to element
+ *   [0,0,0,0] and element strides of the first three dims of a logical
+ *   [batch, seqlen, heads, head_dim] tensor; head_dim is contiguous (stride 1).
+ *   Strided views (e.g. the .transpose(1, 2) views of issue #1402) are fine.
+ *   Every data pointer must be 16-byte aligned and every stride a multiple of
+ *   8 elements (16 bytes), so rows can be moved with 16-byte accesses.
+ * - Ownership: the caller owns every buffer.  The library allocates no device
+ *   or host memory on any call; the KV-cache path uses a caller-provided
+ *   workspace sized by attn_fwd_kvcache_workspace_size().
+ * - Read-only inputs (q, k, v, k_new, v_new, cos/sin, cache_seqlens) may alias
+ *   one another (issue #1402 passes one tensor as q, k and v).  out, lse, the
+ *   caches and the workspace must not alias any other argument.
+ * - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *   stream) and the call returns without waiting.
+ * - Errors: a non-zero return means nothing was enqueued (except
+ *   ATTN_E_HIP, a failed launch); attn_last_error() returns a thread-local
+ *   message describing the last failure of the calling thread.
+ * - Supported: dtype fp16 or bf16 (outputs in the input dtype, accumulation
+ *   in fp32); (Dqk, Dv) in {(16,16), (64,64), (128,128), (192,128)};
+ *   Hq a multiple of Hkv (q head h reads kv head h / (Hq/Hkv)).
+ * - softmax_scale: a NaN value selects 1/sqrt(Dqk); any other value,
+ *   zero included, is used as given.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_dtype { ATTN_DTYPE_F16 = 0, ATTN_DTYPE_BF16 = 1 } attn_dtype;
+
+enum {
+  ATTN_OK = 0,
+  ATTN_E_NULL = -1,        /* a required pointer is NULL                        */
+  ATTN_E_SHAPE = -2,       /* inconsistent or non-positive sizes                */
+  ATTN_E_UNSUPPORTED = -3, /* valid but not implemented (head dims, dtype)      */
+  ATTN_E_ALIGN = -4,       /* pointer not 16-byte aligned / stride not x8       */
+  ATTN_E_WORKSPACE = -5,   /* workspace missing or smaller than required        */
+  ATTN_E_OVERFLOW = -6,    /* scalar cache_seqlens + Snew exceeds the capacity  */
+  ATTN_E_HIP = -7          /* a HIP launch failed                               */
+};
+
+typedef struct attn_tensor4 {
+  void* data;        /* device pointer to element [0,0,0,0]                 */
+  int64_t stride_b;  /* elements between consecutive batch entries          */
+  int64_t stride_s;  /* elements between consecutive sequence positions     */
+  int64_t stride_h;  /* elements between consecutive heads                  */
+} attn_tensor4;
+
+/* ---------------------------------------------------------------- attn_fwd
+ * q   [B, Sq, Hq,  Dqk]   read
+ * k   [B, Sk, Hkv, Dqk]   read
+ * v   [B, Sk, Hkv, Dv ]   read
+ * out [B, Sq, Hq,  Dv ]   written
+ * lse [B, Hq, Sq] fp32, contiguous, written when non-NULL: natural-log
+ *     sum of exp(scale * q.k) over the allowed keys (-inf for a row with none).
+ * causal: key j is allowed for query i iff j <= i + Sk - Sq (bottom-right
+ *     alignment, i.e. j <= i when Sq == Sk); a row with no allowed key
+ *     produces zeros.
+ */
+typedef struct attn_fwd_params {
+  attn_dtype dtype;
+  int B, Sq, Sk, Hq, Hkv, Dqk, Dv;
+  attn_tensor4 q, k, v, out;
+  float* lse;
+  int causal;
+  float softmax_scale;
+} attn_fwd_params;
+
+int attn_fwd(const attn_fwd_params* p, void* stream);
+
+/* -------------------------------------------------------- attn_fwd_kvcache
+ * q       [B, Sq, Hq, Dqk]            read
+ * k_cache [B, capacity, Hkv, Dqk]     read; rows [c_b, c_b + Snew) written
+ * v_cache [B, capacity, Hkv, Dv]      read; rows [c_b, c_b + Snew) written
+ * k_new   [B, Snew, Hkv, Dqk]         read (data NULL iff Snew == 0)
+ * v_new   [B, Snew, Hkv, Dv]          read (data NULL iff Snew == 0)
+ * out     [B, Sq, Hq, Dv]             written
+ * lse     [B, Hq, Sq] fp32 contiguous written when non-NULL
+ *
+ * c_b = cache_seqlens[b] (device int32 [B]) when cache_seqlens is non-NULL,
+ * else cache_seqlens_scalar for every batch.  Snew is 0 or Sq.  Query token i
+ * of batch b sits at absolute position c_b + i; with causal set it attends
+ * keys j <= c_b + i, otherwise all keys j < c_b + Snew.  Cache rows at or
+ * past c_b + Snew are never read, so their content (NaN included) does not
+ * matter, and rows outside [c_b, c_b + Snew) are never written.
+ *
+ * Rotary embedding (when rotary_cos and rotary_sin are non-NULL): tables
+ * [seqlen_ro, rotary_dim/2] in the working dtype, contiguous.  q and k_new
+ * (never v, never the existing cache) are rotated at their absolute
+ * positions; dims >= rotary_dim pass through.  Pairs are (j, j + rd/2), or
+ * (2j, 2j+1) when rotary_interleaved.  Each rotated value is
+ * x1*cos - x2*sin (resp. x1*sin + x2*cos) rounded once to fp32 and then to
+ * the dtype (round-to-nearest-even); the cache receives exactly that value.
+ *
+ * Device-side preconditions (not checked unless the environment variable
+ * ATTN_CHECK=1 is set, which makes the call copy cache_seqlens to the host
+ * and validate them synchronously): 0 <= c_b <= capacity - Snew and, with
+ * rotary tables, c_b + max(Sq, Snew) <= seqlen_ro.
+ *
+ * workspace: device memory of at least attn_fwd_kvcache_workspace_size(p)
+ * bytes, 256-byte aligned (NULL allowed when that size is 0); its content on
+ * entry is irrelevant.  num_splits: 0 picks the split count of the
+ * single-token decode path automatically; a positive value forces it.
+ */
+typedef struct attn_kvcache_params {
+  attn_dtype dtype;
+  int B, Sq, Hq, Hkv, Dqk, Dv, capacity, Snew;
+  attn_tensor4 q, k_cache, v_cache, k_new, v_new, out;
+  int cache_seqlens_scalar;
+  const int32_t* cache_seqlens;
+  const void* rotary_cos;
+  const void* rotary_sin;
+  int rotary_dim, seqlen_ro, rotary_interleaved;
+  int causal;
+  float softmax_scale;
+  float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+  int num_splits;
+} attn_kvcache_params;
+
+size_t attn_fwd_kvcache_workspace_size(const attn_kvcache_params* p);
+int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream);
+
+/* -------------------------------------------------------------- rope_apply
+ * x   [B, S, H, D]  read
+ * out [B, S, H, D]  written; may be the same memory as x (in place)
+ * Token s of batch b is at position off_b + s with off_b = offsets[b]
+ * (device int32 [B]) when offsets is non-NULL, else offset_scalar.
+ * Same pairing and rounding as the kvcache rotation; conjugate rotates by
+ * the opposite angle (sin -> -sin).  Precondition: off_b + S <= seqlen_ro.
+ */
+typedef struct attn_rope_params {
+  attn_dtype dtype;
+  int B, S, H, D;
+  attn_tensor4 x, out;
+  const void* cos;
+  const void* sin;
+  int rotary_dim, seqlen_ro, interleaved, conjugate;
+  int offset_scalar;
+  const int32_t* offsets;
+} attn_rope_params;
+
+int rope_apply(const attn_rope_params* p, void* stream);
+
+/* ------------------------------------------------------------ host helpers
+ * The attn_validate_* functions run the argument checks of the matching
+ * entry point on the host only (no HIP call, nothing enqueued) and return
+ * the status that entry point would return.
+ */
+int attn_validate_fwd(const attn_fwd_params* p);
+int attn_validate_kvcache(const attn_kvcache_params* p);
+int attn_validate_rope(const attn_rope_params* p);
+const char* attn_last_error(void);
+int attn_abi_version(void);  /* 1 */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTN_H_ */

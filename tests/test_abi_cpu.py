@@ -1,0 +1,199 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load, export every function include/attn.h declares, share
+torch's HIP runtime, and reject every malformed argument on the host before
+anything is enqueued.  attn_validate_* make no HIP call, so CPU tensors'
+addresses stand in for device pointers here (they are never dereferenced).
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+import torch
+
+import exact_attention_qk_amd as E
+from exact_attention_qk_amd import AttnError
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_functions_are_all_exported():
+    names = _declared_functions()
+    assert set(names) == set(E.EXPORTED), names
+    lib = ctypes.CDLL(E.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert E.lib().attn_abi_version() == 1
+
+
+def test_single_hip_runtime_in_process():
+    maps = open("/proc/self/maps").read().splitlines()
+    libs = {l.split()[-1] for l in maps if "libamdhip64" in l}
+    assert len(libs) == 1, libs
+
+
+def _t(shape, dtype=torch.float16):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _fwd(B=2, Sq=8, Sk=8, Hq=4, Hkv=2, Dqk=64, Dv=64, dtype=torch.float16, **kw):
+    q, k, v = _t((B, Sq, Hq, Dqk), dtype), _t((B, Sk, Hkv, Dqk), dtype), _t((B, Sk, Hkv, Dv), dtype)
+    out = _t((B, Sq, Hq, Dv), dtype)
+    return E.fwd_params(q, k, v, out, **kw), (q, k, v, out)
+
+
+def _code_fwd(p):
+    return E.lib().attn_validate_fwd(ctypes.byref(p))
+
+
+def test_validate_fwd_ok_and_errors():
+    p, keep = _fwd()
+    assert _code_fwd(p) == 0
+    p, keep = _fwd(Hq=3, Hkv=2)
+    assert _code_fwd(p) == -2
+    assert b"multiple" in E.lib().attn_last_error()
+    p, keep = _fwd(Dqk=96, Dv=96)
+    assert _code_fwd(p) == -3
+    p, keep = _fwd(Dqk=128, Dv=64)
+    assert _code_fwd(p) == -3
+    p, keep = _fwd()
+    p.q.data = None
+    assert _code_fwd(p) == -1
+    p, keep = _fwd()
+    p.k.data = p.k.data + 2
+    assert _code_fwd(p) == -4
+    p, keep = _fwd()
+    p.v.stride_s = 100
+    assert _code_fwd(p) == -4
+    p, keep = _fwd()
+    p.dtype = 7
+    assert _code_fwd(p) == -3
+    # empty problems are valid no-ops
+    p, keep = _fwd(Sq=0)
+    assert _code_fwd(p) == 0
+    p, keep = _fwd(Sk=0)
+    p.k.data = None
+    p.v.data = None
+    assert _code_fwd(p) == 0
+
+
+def test_binding_rejects_other_dtypes_before_any_launch():
+    q = torch.zeros(1, 4, 1, 64)
+    with pytest.raises(AttnError):
+        E.attn_fwd(q, q, q)
+
+
+def _kv(B=2, Sq=1, Hq=8, Hkv=2, D=128, cap=64, snew=1, seqlens=5, rotary=0, dtype=torch.bfloat16,
+        **kw):
+    q = _t((B, Sq, Hq, D), dtype)
+    kc, vc = _t((B, cap, Hkv, D), dtype), _t((B, cap, Hkv, D), dtype)
+    kn = _t((B, snew, Hkv, D), dtype) if snew else None
+    vn = _t((B, snew, Hkv, D), dtype) if snew else None
+    cos = sin = None
+    if rotary:
+        cos, sin = _t((cap, rotary // 2), dtype), _t((cap, rotary // 2), dtype)
+    out = _t((B, Sq, Hq, D), dtype)
+    p = E.kvcache_params(q, kc, vc, kn, vn, cos, sin, seqlens, True, None, False, out, None, None,
+                         kw.get("num_splits", 0))
+    return p, (q, kc, vc, kn, vn, cos, sin, out)
+
+
+def _code_kv(p):
+    return E.lib().attn_validate_kvcache(ctypes.byref(p))
+
+
+def test_validate_kvcache_workspace_and_overflow():
+    p, keep = _kv()
+    need = E.kvcache_workspace_size(p)
+    assert need > 0                                     # decode path needs split partials
+    assert _code_kv(p) == -5                            # no workspace given
+    ws = torch.zeros(need + 512, dtype=torch.uint8)
+    base = ws.data_ptr() + (-ws.data_ptr()) % 256
+    p.workspace, p.workspace_bytes = base, need
+    assert _code_kv(p) == 0
+    p.workspace_bytes = need - 1
+    assert _code_kv(p) == -5
+    p.workspace, p.workspace_bytes = base + 16, need
+    assert _code_kv(p) == -4
+    p2, keep2 = _kv(seqlens=64)                          # 64 + 1 > capacity 64
+    assert _code_kv(p2) == -6
+    p3, keep3 = _kv(seqlens=-1)
+    assert _code_kv(p3) == -2
+    p4, keep4 = _kv(snew=0)
+    p4.Snew = 1                                         # k_new NULL with Snew = 1
+    p4.workspace, p4.workspace_bytes = base, need
+    assert _code_kv(p4) == -1
+
+
+def test_validate_kvcache_rotary_args():
+    p, keep = _kv(rotary=64)
+    assert p.rotary_dim == 64 and p.seqlen_ro == 64
+    need = E.kvcache_workspace_size(p)
+    ws = torch.zeros(need + 512, dtype=torch.uint8)
+    p.workspace = ws.data_ptr() + (-ws.data_ptr()) % 256
+    p.workspace_bytes = need
+    assert _code_kv(p) == 0
+    p.rotary_dim = 63
+    assert _code_kv(p) == -2
+    p.rotary_dim = 256
+    assert _code_kv(p) == -2
+    p.rotary_dim = 64
+    p.rotary_sin = None
+    assert _code_kv(p) == -1
+    p, keep = _kv(rotary=64, seqlens=63)                 # position 63 + 1 token > 64 rows
+    p.seqlen_ro = 63
+    assert _code_kv(p) == -2
+
+
+def test_kvcache_workspace_plan():
+    # decode path: partials for every (batch, kv head, split, row) plus rotated q
+    p, keep = _kv(B=8, Hq=32, Hkv=8, D=128, cap=8192, rotary=128)
+    need = E.kvcache_workspace_size(p)
+    split = 128
+    nsp = 8192 // split
+    R = 4
+    q_rot = 8 * 1 * 32 * 128 * 2
+    expect = q_rot + 8 * 8 * nsp * R * 128 * 4
+    expect = ((expect + 255) // 256) * 256 + ((8 * 8 * nsp * R * 2 * 4 + 255) // 256) * 256
+    assert need == expect
+    # forcing one split
+    p.num_splits = 1
+    assert E.kvcache_workspace_size(p) == q_rot + 8 * 8 * 1 * R * 128 * 4 + 8 * 8 * R * 2 * 4
+    # chunked prefill (many query rows): only the rotated q copy
+    p, keep = _kv(B=4, Sq=512, Hq=16, Hkv=16, D=128, cap=4096, snew=512, rotary=64)
+    assert E.kvcache_workspace_size(p) == 4 * 512 * 16 * 128 * 2
+    p, keep = _kv(B=4, Sq=512, Hq=16, Hkv=16, D=128, cap=4096, snew=512)
+    assert E.kvcache_workspace_size(p) == 0
+
+
+def test_validate_rope():
+    x = _t((2, 5, 3, 64))
+    cos, sin = _t((16, 16)), _t((16, 16))
+    p = E.rope_params(x, cos, sin, 3, False, False, x)
+    assert E.lib().attn_validate_rope(ctypes.byref(p)) == 0
+    p = E.rope_params(x, cos, sin, 12, False, False, x)      # 12 + 5 > 16 rows
+    assert E.lib().attn_validate_rope(ctypes.byref(p)) == -2
+    p = E.rope_params(x, cos, sin, 0, False, False, x)
+    p.rotary_dim = 65
+    assert E.lib().attn_validate_rope(ctypes.byref(p)) == -2
+    p = E.rope_params(x, cos, sin, 0, False, False, x)
+    p.cos = None
+    assert E.lib().attn_validate_rope(ctypes.byref(p)) == -1
+
+
+def test_kvcache_binding_requires_explicit_interleave_flag():
+    q = torch.zeros(1, 1, 2, 64, dtype=torch.float16)
+    cos = torch.zeros(4, 32, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        E.attn_fwd_kvcache(q, q, q, rotary_cos=cos, rotary_sin=cos)

@@ -1,0 +1,354 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Bars (stated for this method): outputs within max-abs 2e-3 (fp16) or 1.5e-2
+(bf16) of the fp64 oracle, fp32 accumulation inside; KV-cache contents and
+the positions written bit-exact; rotary outputs bit-exact (they are a single
+rounding of an exactly-defined value).  Inputs are seeded (workloads.py).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attention_ref, dtype_bits, kvcache_ref, rope_ref, to_f64
+
+pytestmark = pytest.mark.gpu
+TOL = {"fp16": 2e-3, "bf16": 1.5e-2}
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print("\n[gpu-case] %s" % request.node.nodeid, flush=True)
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    yield
+    torch.cuda.synchronize()
+
+
+def E():
+    import exact_attention_qk_amd as mod
+    return mod
+
+
+def dev(t):
+    return None if t is None else t.to(DEV)
+
+
+def maxabs(gpu_out, ref):
+    g = to_f64(gpu_out.float().cpu())
+    assert np.isfinite(g).all(), "non-finite output"
+    return float(np.max(np.abs(g - ref))) if g.size else 0.0
+
+
+def guarded_empty(shape, dtype, fill=-7.0):
+    """A tensor view with canary elements before and after it in the same allocation."""
+    n = int(np.prod(shape))
+    buf = torch.full((n + 256,), fill, dtype=dtype, device=DEV)
+    return buf, buf[128:128 + n].view(shape)
+
+
+def canaries_intact(buf, n, fill=-7.0):
+    b = buf.float().cpu()
+    return bool((b[:128] == fill).all() and (b[128 + n:] == fill).all())
+
+
+# ---------------------------------------------------------------- attn_fwd
+
+DIMS = [(16, 16), (64, 64), (128, 128), (192, 128)]
+
+
+def _fwd_check(case, sample_rows=None, tol=None, return_lse=False):
+    q, k, v = dev(case.q), dev(case.k), dev(case.v)
+    B, Sq, Hq, _ = q.shape
+    Dv = v.shape[3]
+    buf, out = guarded_empty((B, Sq, Hq, Dv), q.dtype)
+    res = E().attn_fwd(q, k, v, causal=case.causal, softmax_scale=case.softmax_scale, out=out,
+                       return_lse=return_lse)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf, out.numel())
+    qf, kf, vf = to_f64(case.q), to_f64(case.k), to_f64(case.v)
+    Sk = kf.shape[1]
+    if sample_rows is None:
+        ref, lse = attention_ref(qf, kf, vf, causal=case.causal, softmax_scale=case.softmax_scale)
+        got = out
+    else:
+        rows = np.asarray(sample_rows)
+        pos = np.tile(rows + Sk - Sq, (B, 1))
+        ref, lse = attention_ref(qf[:, rows], kf, vf, causal=case.causal,
+                                 softmax_scale=case.softmax_scale, q_pos=pos)
+        got = out[:, torch.as_tensor(rows, device=DEV)]
+    err = maxabs(got, ref)
+    assert err <= (tol or TOL[case.dtype]), "max abs err %.3e" % err
+    if return_lse:
+        l = res[1].cpu().double().numpy()
+        if sample_rows is not None:
+            l = l[:, :, rows]
+        fin = np.isfinite(lse)
+        assert np.array_equal(fin, np.isfinite(l))
+        assert np.max(np.abs(l[fin] - lse[fin])) < 2e-3
+    return err
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("dqk,dv", DIMS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_multi_tile_ragged(dtype, dqk, dv, causal):
+    # 200 rows/keys: two 128-row query tiles and four 64-key tiles, ragged tails; GQA 4:2.
+    case = W.random_fwd(2, 200, 200, 4, 2, dqk, dv, dtype, causal, seed=dqk + causal)
+    _fwd_check(case, return_lse=True)
+
+
+@pytest.mark.parametrize("sq,sk", [(100, 333), (300, 77), (1, 129), (129, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_sq_ne_sk(sq, sk, causal):
+    # causal uses bottom-right alignment; rows with no allowed key give 0 / -inf lse
+    case = W.random_fwd(1, sq, sk, 2, 1, 64, 64, "fp16", causal, seed=sq * 7 + sk)
+    _fwd_check(case, return_lse=True)
+
+
+def test_fwd_strided_transposed_views():
+    g = torch.Generator().manual_seed(5)
+    q = torch.randn(2, 4, 150, 128, generator=g).to(torch.bfloat16)
+    k = torch.randn(2, 4, 150, 128, generator=g).to(torch.bfloat16)
+    v = torch.randn(2, 4, 150, 128, generator=g).to(torch.bfloat16)
+    case = W.FwdCase("strided", "bf16", q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2),
+                     True, None)
+    assert not case.q.is_contiguous()
+    _fwd_check(case)
+
+
+def test_fwd_empty_and_no_keys():
+    q = torch.randn(1, 5, 2, 64, device=DEV).half()
+    k = torch.zeros(1, 0, 2, 64, device=DEV).half()
+    out, lse = E().attn_fwd(q, k, k, return_lse=True)
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all() and torch.isinf(lse).all()
+    e = E().attn_fwd(q[:, :0], q, q)
+    assert e.shape[1] == 0
+
+
+def test_fwd_softmax_scale_zero_is_mean():
+    case = W.random_fwd(1, 64, 96, 2, 2, 64, 64, "fp16", False, seed=3, softmax_scale=0.0)
+    _fwd_check(case)
+
+
+def test_fwd_ones_v_gives_ones():
+    # probabilities sum to one: V = 1 gives O = 1 for every row
+    case = W.random_fwd(1, 130, 130, 2, 1, 128, 128, "bf16", True, seed=4)
+    case.v = torch.ones_like(case.v)
+    out = E().attn_fwd(dev(case.q), dev(case.k), dev(case.v), causal=True)
+    torch.cuda.synchronize()
+    assert (out.float() - 1).abs().max().item() <= 2 ** -7
+
+
+def test_fwd_first_causal_row_is_v0_bitwise():
+    case = W.random_fwd(2, 256, 256, 4, 4, 64, 64, "fp16", True, seed=8)
+    out = E().attn_fwd(dev(case.q), dev(case.k), dev(case.v), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, 0].cpu(), case.v[:, 0])
+
+
+def test_skill_page_fp16_accuracy_check():
+    # Workflow 1 Step 4 of the skill page: fp16, B=1, H=8, S=512, D=64, max diff below 1e-3.
+    case = W.random_fwd(1, 512, 512, 8, 8, 64, 64, "fp16", False, seed=0, softmax_scale=1 / 8)
+    assert _fwd_check(case) < 1e-3
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_workload_fwd_d64_full(causal):
+    case = W.fwd_d64(causal)
+    _fwd_check(case, return_lse=True)
+
+
+def test_workload_fwd_asym_sampled_rows():
+    case = W.fwd_asym()
+    rows = sorted(set(list(range(0, 8)) + list(range(4088, 4096)) +
+                      list(np.random.default_rng(0).choice(4096, 112, replace=False))))
+    _fwd_check(case, sample_rows=rows)
+
+
+# ---------------------------------------------------------------- kvcache
+
+def _kv_run(case, num_splits=0, return_lse=True, share_q=False):
+    """Run the HIP kvcache path on device copies; returns (out, lse, k_cache, v_cache)."""
+    q = dev(case.q)
+    if share_q:
+        kn = vn = q                  # one tensor passed as q, k and v (issue #1402)
+    else:
+        kn, vn = dev(case.k_new), dev(case.v_new)
+    kc, vc = dev(case.k_cache), dev(case.v_cache)
+    cs = dev(case.cache_seqlens) if isinstance(case.cache_seqlens, torch.Tensor) else case.cache_seqlens
+    out, lse = E().attn_fwd_kvcache(q, kc, vc, kn, vn, rotary_cos=dev(case.rotary_cos),
+                                    rotary_sin=dev(case.rotary_sin), cache_seqlens=cs,
+                                    causal=case.causal, softmax_scale=case.softmax_scale,
+                                    rotary_interleaved=case.rotary_interleaved,
+                                    num_splits=num_splits, return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse, kc, vc
+
+
+def _kv_oracle(case):
+    f = to_f64
+    B = case.q.shape[0]
+    lens = W.seqlens_list(case.cache_seqlens, B)
+    return kvcache_ref(f(case.q), f(case.k_cache), f(case.v_cache),
+                       None if case.k_new is None else f(case.k_new),
+                       None if case.v_new is None else f(case.v_new),
+                       lens if isinstance(case.cache_seqlens, torch.Tensor) else case.cache_seqlens,
+                       dtype=case.dtype,
+                       rotary_cos=None if case.rotary_cos is None else f(case.rotary_cos),
+                       rotary_sin=None if case.rotary_sin is None else f(case.rotary_sin),
+                       rotary_interleaved=case.rotary_interleaved, causal=case.causal,
+                       softmax_scale=case.softmax_scale)
+
+
+def _bits_equal(gpu_cache, ref_cache, dtype):
+    g = gpu_cache.cpu().view(torch.int16).numpy().view(np.uint16)
+    r = dtype_bits(ref_cache, dtype)
+    same = (g == r)
+    # NaN sentinels compare as NaN == NaN here: both sides must be NaN
+    nan_ref = np.isnan(ref_cache)
+    if nan_ref.any():
+        gv = to_f64(gpu_cache.float().cpu())
+        same = same | (nan_ref & np.isnan(gv))
+    return bool(same.all())
+
+
+def _kv_check(case, num_splits=0, share_q=False):
+    out, lse, kc, vc = _kv_run(case, num_splits, share_q=share_q)
+    ref, rlse, rkc, rvc = _kv_oracle(case)
+    err = maxabs(out, ref)
+    assert err <= TOL[case.dtype], "max abs err %.3e" % err
+    assert _bits_equal(kc, rkc, case.dtype), "k_cache differs from the oracle"
+    assert _bits_equal(vc, rvc, case.dtype), "v_cache differs from the oracle"
+    l = lse.cpu().double().numpy()
+    fin = np.isfinite(rlse)
+    assert np.array_equal(fin, np.isfinite(l))
+    assert np.max(np.abs(l[fin] - rlse[fin])) < 2e-3
+    return out, err
+
+
+def test_workload_kvcache_empty():
+    case = W.kvcache_empty()
+    out, _ = _kv_check(case, share_q=True)
+    # an empty cache with cache_seqlens=0 equals plain attention on the new tokens
+    q = dev(case.q)
+    plain = E().attn_fwd(q, q, q)
+    torch.cuda.synchronize()
+    diff = (plain.float() - out.float()).abs().max().item()
+    assert diff <= 2 ** -11, diff       # at most one fp16 ulp of values below 1
+
+
+def test_workload_decode_gqa():
+    _kv_check(W.decode_gqa())
+
+
+def test_workload_chunked_prefill():
+    _kv_check(W.chunked_prefill())
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("dqk,dv", DIMS)
+def test_kvcache_decode_nan_tail(dtype, dqk, dv):
+    case = W.random_kvcache(3, 1, 8, 2, dqk, dv, 300, dtype, snew=1, seqlens=[0, 37, 298],
+                            rotary_dim=dqk // 2, interleaved=dqk == 64, seed=dqk,
+                            tail_fill=float("nan"))
+    _kv_check(case)
+
+
+@pytest.mark.parametrize("rot", [0, 64])
+def test_kvcache_chunk_nan_tail(rot):
+    case = W.random_kvcache(2, 70, 4, 4, 128, 128, 400, "bf16", snew=70, seqlens=[0, 201],
+                            rotary_dim=rot, interleaved=True, seed=11, tail_fill=float("nan"))
+    _kv_check(case)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_kvcache_decode_two_tokens_full_rows(causal):
+    # Sq = 2 with 8 q heads per kv head: R = 16 rows, the decode path's maximum
+    case = W.random_kvcache(2, 2, 16, 2, 64, 64, 256, "fp16", snew=2, seqlens=[5, 190],
+                            rotary_dim=64, causal=causal, seed=13)
+    _kv_check(case)
+
+
+def test_kvcache_scalar_and_tensor_seqlens_agree():
+    a = W.random_kvcache(2, 1, 4, 1, 128, 128, 512, "bf16", snew=1, seqlens=[300, 300],
+                         rotary_dim=128, seed=15)
+    b = W.random_kvcache(2, 1, 4, 1, 128, 128, 512, "bf16", snew=1, seqlens=[300, 300],
+                         rotary_dim=128, seed=15, seqlens_as_tensor=False)
+    oa, _, ka, _ = _kv_run(a)
+    ob, _, kb, _ = _kv_run(b)
+    assert torch.equal(oa, ob) and torch.equal(ka, kb)
+    _kv_check(b)
+
+
+def test_kvcache_one_split_matches_auto():
+    case = W.random_kvcache(2, 1, 8, 2, 128, 128, 2048, "bf16", snew=1, seqlens=[1500, 2000],
+                            seed=17)
+    o1, _, _, _ = _kv_run(case, num_splits=1)
+    oa, _, _, _ = _kv_run(case, num_splits=0)
+    assert (o1.float() - oa.float()).abs().max().item() <= 2 ** -6
+    _kv_check(case, num_splits=1)
+    _kv_check(case, num_splits=5)
+
+
+def test_kvcache_gqa_equals_repeated_mha():
+    case = W.random_kvcache(2, 1, 8, 2, 64, 64, 256, "fp16", snew=1, seqlens=[100, 200], seed=19)
+    o_gqa, _, _, _ = _kv_run(case)
+    rep = W.KVCacheCase("rep", "fp16", case.q, case.k_cache.repeat_interleave(4, dim=2),
+                        case.v_cache.repeat_interleave(4, dim=2),
+                        case.k_new.repeat_interleave(4, dim=2), case.v_new.repeat_interleave(4, dim=2),
+                        case.cache_seqlens, causal=True)
+    o_mha, _, _, _ = _kv_run(rep)
+    assert (o_gqa.float() - o_mha.float()).abs().max().item() <= 2e-3
+
+
+def test_kvcache_no_new_tokens():
+    case = W.random_kvcache(2, 1, 4, 2, 128, 128, 128, "bf16", snew=0, seqlens=[1, 77],
+                            rotary_dim=128, seed=21)
+    _kv_check(case)
+
+
+def test_kvcache_fused_rope_equals_unfused():
+    case = W.random_kvcache(2, 40, 4, 2, 128, 128, 256, "bf16", snew=40, seqlens=[3, 150],
+                            rotary_dim=64, interleaved=False, seed=23)
+    out_f, _, kc_f, vc_f = _kv_run(case)
+    mod = E()
+    cs = dev(case.cache_seqlens)
+    q_r = mod.rope_apply(dev(case.q), dev(case.rotary_cos), dev(case.rotary_sin), cs, False)
+    k_r = mod.rope_apply(dev(case.k_new), dev(case.rotary_cos), dev(case.rotary_sin), cs, False)
+    kc, vc = dev(case.k_cache), dev(case.v_cache)
+    out_u = mod.attn_fwd_kvcache(q_r, kc, vc, k_r, dev(case.v_new), cache_seqlens=cs, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(kc_f, kc) and torch.equal(vc_f, vc)
+    assert torch.equal(out_f, out_u)
+
+
+# ---------------------------------------------------------------- rope_apply
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("interleaved", [False, True])
+@pytest.mark.parametrize("rd", [32, 128])
+def test_rope_apply_bit_exact(dtype, interleaved, rd):
+    tdt = W.DTYPES[dtype]
+    g = torch.Generator().manual_seed(rd + interleaved)
+    x = torch.randn(3, 50, 4, 128, generator=g).to(tdt)
+    cos, sin = W.rope_tables(512, rd, 10000.0, tdt)
+    offs = torch.tensor([0, 17, 400], dtype=torch.int32)
+    mod = E()
+    for conj in (False, True):
+        y = mod.rope_apply(dev(x), dev(cos), dev(sin), dev(offs), interleaved, conj)
+        torch.cuda.synchronize()
+        pos = offs.numpy()[:, None] + np.arange(50)[None, :]
+        ref = rope_ref(to_f64(x), to_f64(cos), to_f64(sin), pos, rotary_dim=rd,
+                       interleaved=interleaved, conjugate=conj, dtype=dtype)
+        assert _bits_equal(y, ref, dtype)
+    # in place, scalar offset
+    xd = dev(x)
+    mod.rope_apply(xd, dev(cos), dev(sin), 5, interleaved, inplace=True)
+    torch.cuda.synchronize()
+    ref = rope_ref(to_f64(x), to_f64(cos), to_f64(sin), 5 + np.tile(np.arange(50), (3, 1)),
+                   rotary_dim=rd, interleaved=interleaved, dtype=dtype)
+    assert _bits_equal(xd, ref, dtype)
