@@ -7,21 +7,32 @@
 // Quick start on IO-aware tiling; Workflow 1 Step 2 for the definition it
 // must equal).
 //
-// Work decomposition (one workgroup = NW waves of 64 lanes):
-//  * a workgroup owns BM = 32*NW query rows of one (batch, q head); each wave
-//    owns 32 rows and keeps their Q fragment in registers for the whole pass;
-//  * K/V tiles of BN = 64 keys are staged global -> registers -> LDS, the next
-//    tile's global loads in flight while the current tile is consumed;
-//  * S^T = K Q^T on v_mfma_f32_32x32x16 (K from LDS, Q from registers), so a
-//    lane owns one query row: the row max needs a single lane^32 exchange and
-//    the row sum none until the end;
-//  * the K rows fed to the MFMA are permuted so that each lane's 8-score
-//    groups cover 8 consecutive keys; those scores, rounded to the input type,
-//    are directly the B operand of O^T += V^T P^T, whose A operand V^T is read
-//    from the row-major V tile with ds_read_b64_tr_b16;
-//  * causal: each wave skips 32-key blocks that lie entirely above its rows'
-//    diagonal and masks only blocks that cross it; key rows past the key
-//    length are never loaded (zero-filled) and masked;
+// Work decomposition.  A workgroup owns BM = NR * 32 * RB query rows of one
+// (batch, q head) and is made of NS key-split groups of NR waves:
+//  * every wave owns 32*RB query rows (RB MFMA row blocks) and keeps their Q
+//    fragments in registers; the NS groups hold the same rows and walk
+//    disjoint key tiles (tile t goes to group t % NS), which multiplies the
+//    waves per CU on small problems; the groups' partial results are merged
+//    exactly through LDS at the end;
+//  * each group double-buffers its 64-key K/V tiles in LDS with direct
+//    global->LDS loads (global_load_lds_dwordx4): the next tile streams in
+//    while the current one is consumed, without staging registers.  Rows past
+//    the key length are fetched from the last valid row (so stale or NaN cache
+//    content is never read) and masked;
+//  * S^T = K Q^T on v_mfma_f32_32x32x16: one K fragment read from LDS feeds RB
+//    MFMAs, and a lane owns one query row, so the row max needs one lane^32
+//    exchange and the row sum none until the end;
+//  * the K rows fed to the MFMA are permuted so each lane's 8-score groups
+//    cover 8 consecutive keys; rounded to the input type those scores are
+//    directly the B operand of O^T += V^T P^T, whose A operand V^T comes from
+//    the row-major V tile through ds_read_b64_tr_b16;
+//  * online softmax: P = exp2(s*c - m*c) with one FMA per score (c = scale *
+//    log2 e); the running max used as reference is only raised when a row's
+//    max exceeds it by more than 2^8, so the O rescale is rare and P stays
+//    below 256; the row sum is accumulated from the packed P with v_dot2, so
+//    numerator and denominator use the same rounded weights;
+//  * causal: waves skip 32-key blocks above their rows' diagonal and mask only
+//    blocks that cross it;
 //  * epilogue: O / l rounded to the output type, staged through LDS so each
 //    lane stores 16 contiguous bytes of an output row.
 #include "device_common.hpp"
@@ -30,55 +41,83 @@
 
 namespace attn {
 
-constexpr int BN = 64;
+constexpr float kLazyRescale = 8.0f;  // log2 units: P may grow to 2^8 before a rescale
 
-// MFMA row m of a 32-key block -> key offset inside the block (see header).
 __device__ __forceinline__ int key_perm(int m) {
   int a = m >> 3, hh = (m >> 2) & 1, b = m & 3;
   return 16 * (a >> 1) + 8 * hh + 4 * (a & 1) + b;
 }
 
-template <class T, int DQK, int DV, bool CAUSAL, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void tile_attn_kernel(AttnArgs a) {
-  constexpr int NT = 64 * NW;
-  constexpr int BM = 32 * NW;
-  constexpr int CK = DQK / 8;             // 16-byte chunks per K row
-  constexpr int CV = DV / 8;              // 16-byte chunks per V row
-  constexpr int KSTEPS = DQK / 16;        // MFMA k-steps for S
-  constexpr int DVB = (DV + 31) / 32;     // 32-wide output blocks
-  constexpr int KPT = (BN * CK + NT - 1) / NT;
-  constexpr int VPT = (BN * CV + NT - 1) / NT;
-  constexpr int OSTR = DV + 8;            // padded row stride of the output staging tile
-  constexpr int LDS_KV = BN * (DQK + DV);
-  constexpr int LDS_O = NW * 32 * OSTR;
-  constexpr int LDS_ELEMS = LDS_KV > LDS_O ? LDS_KV : LDS_O;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
-  uint16_t* lds_k = lds;
-  uint16_t* lds_v = lds + BN * DQK;
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+template <class T>
+__device__ __forceinline__ uint32_t pack_p(float a, float b);
+template <>
+__device__ __forceinline__ uint32_t pack_p<F16>(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+template <>
+__device__ __forceinline__ uint32_t pack_p<BF16>(float a, float b) {
+  return BF16::pack2(a, b);
+}
+template <class T>
+__device__ __forceinline__ float dot2_sum(uint32_t p, float acc);
+template <>
+__device__ __forceinline__ float dot2_sum<F16>(uint32_t p, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), (f16x2){(_Float16)1.f, (_Float16)1.f},
+                                acc, false);
+}
+template <>
+__device__ __forceinline__ float dot2_sum<BF16>(uint32_t p, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p),
+                                         (bf16x2){(__bf16)1.f, (__bf16)1.f}, acc, false);
+}
+
+template <class T, int DQK, int DV, bool CAUSAL, int RB, int NR, int NS, int BN, bool FASTC, int MINW>
+__global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs a) {
+  constexpr int NKB = BN / 32;                           // 32-key MFMA blocks per tile
+  constexpr int RW = 32 * RB;
+  constexpr int BM = NR * RW;
+  constexpr int CK = DQK / 8;
+  constexpr int CV = DV / 8;
+  constexpr int KSTEPS = DQK / 16;
+  constexpr int DVB = (DV + 31) / 32;
+  constexpr int KT = BN * DQK;
+  constexpr int VT = BN * DV;
+  constexpr int STAGE = KT + VT;                          // elements
+  constexpr int LDS_KV = NS * 2 * STAGE * 2;              // bytes
+  constexpr int MERGE_O = (NS - 1) * NR * RB * DVB * 16 * 64;   // floats
+  constexpr int MERGE_B = (MERGE_O + (NS - 1) * NR * RB * 2 * 64) * 4;
+  constexpr int OSTR = DV + 8;
+  constexpr int LDS_O = BM * OSTR * 2;
+  constexpr int LDS_BYTES = cmax(LDS_KV, cmax(MERGE_B, LDS_O));
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
+  uint16_t* lds16 = reinterpret_cast<uint16_t*>(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int g = w / NR;          // key-split group
+  const int rw = w - g * NR;     // row wave inside the group
   const int hh = lane >> 5;
 
-  // ---- which (batch, q head, q tile) this workgroup owns
+  // ---- work unit
   int u = blockIdx.x;
-  const int total = gridDim.x;
-  if (a.xcd_remap) {  // consecutive units on one XCD so their K/V stay in its L2
-    int per = total >> 3;
+  if (a.xcd_remap) {
+    const int per = gridDim.x >> 3;
     u = (u & 7) * per + (u >> 3);
   }
   const int nqt = a.num_qtiles;
   const int bh = u / nqt;
   int qt = u - bh * nqt;
-  if (CAUSAL) qt = nqt - 1 - qt;  // heavy tiles first within a (batch, head)
+  if (CAUSAL) qt = nqt - 1 - qt;
   const int b = bh / a.Hq;
   const int hq = bh - b * a.Hq;
   const int hkv = hq / a.group;
 
   int L, off;
   if (a.kvcache) {
-    int cb = a.seqlens ? a.seqlens[b] : a.seqlen_scalar;
+    const int cb = a.seqlens ? a.seqlens[b] : a.seqlen_scalar;
     L = cb + a.Snew;
     off = cb;
   } else {
@@ -90,253 +129,342 @@ __global__ __launch_bounds__(64 * NW, 2) void tile_attn_kernel(AttnArgs a) {
   int kend = L;
   if (CAUSAL) kend = max(0, min(L, off + rows_end));
   const int ntiles = (kend + BN - 1) / BN;
+  const int nit = (ntiles + NS - 1) / NS;
 
-  // per-wave row range
-  const int wr0 = q0 + 32 * w;
-  const int wr1 = min(wr0 + 32, a.Sq);        // exclusive
+  const int wr0 = q0 + rw * RW;
+  const int wr1 = min(wr0 + RW, a.Sq);
   const bool wave_active = wr0 < a.Sq;
-  const int pmin = off + wr0;                  // smallest query position of the wave
-  const int pmax = off + wr1 - 1;              // largest
+  const int pmin = off + wr0;
   int wkend = L;
-  if (CAUSAL) wkend = max(0, min(L, pmax + 1));
+  if (CAUSAL) wkend = max(0, min(L, off + wr1));
 
   const uint16_t* qbase = a.q + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh;
   const uint16_t* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
   const uint16_t* vbase = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
 
-  // ---- Q fragment (B operand of S^T = K Q^T): row l%32, dims 16s + 8h .. +7
-  const int qrow = wr0 + (lane & 31);
-  u32x4 qf[KSTEPS];
+  // ---- tile DMA: tile t of this group into stage s
+  auto issue = [&](int t, int s) {
+    uint16_t* kd = lds16 + (g * 2 + s) * STAGE;
+    uint16_t* vd = kd + KT;
+    const int key0 = t * BN;
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) {
-    qf[s] = (u32x4){0, 0, 0, 0};
-    if (qrow < a.Sq) qf[s] = ldg16(qbase + (int64_t)qrow * a.q_ss + 16 * s + 8 * hh);
+    for (int I = rw; I < NKB * CK / 2; I += NR) {
+      const int P = I * 64 + lane;
+      const int row = P / CK, pos = P - (P / CK) * CK;
+      const int ch = pos ^ swz_k<CK>(row);
+      const int key = min(key0 + row, L - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + (int64_t)key * a.k_ss + ch * 8),
+                                       (LDS_AS void*)(kd + I * 512), 16, 0, 0);
+    }
+#pragma unroll
+    for (int I = rw; I < NKB * CV / 2; I += NR) {
+      const int P = I * 64 + lane;
+      const int row = P / CV, pos = P - (P / CV) * CV;
+      const int ch = pos ^ swz_v<CV>(row);
+      const int key = min(key0 + row, L - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + (int64_t)key * a.v_ss + ch * 8),
+                                       (LDS_AS void*)(vd + I * 512), 16, 0, 0);
+    }
+  };
+
+  // ---- Q fragments (B operand of S^T = K Q^T)
+  u32x4 qf[RB][KSTEPS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int qrow = wr0 + rb * 32 + (lane & 31);
+    const int qr = min(qrow, a.Sq - 1);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[rb][s] = ldg16(qbase + (int64_t)qr * a.q_ss + 16 * s + 8 * hh);
   }
 
-  f32x16 o[DVB];
+  f32x16 o[RB][DVB];
 #pragma unroll
-  for (int i = 0; i < DVB; ++i) o[i] = (f32x16){};
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
-  const float c = a.c;
-  const int qpos = off + qrow;
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int i = 0; i < DVB; ++i) o[rb][i] = (f32x16){};
+  float m_use[RB], l_run[RB];   // m_use in log2 units (score * c)
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_use[rb] = -__builtin_inff();
+    l_run[rb] = 0.f;
+  }
+  const float c = FASTC ? a.c : 1.f;
+  const float cpre = a.c;   // general path: scores are multiplied by c first
 
-  // ---- tile loader (global -> registers -> LDS)
-  u32x4 kreg[KPT], vreg[VPT];
-  auto load_tile = [&](int t) {
-    const int key0 = t * BN;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      int id = i * NT + tid;
-      int row = id / CK, ch = id - (id / CK) * CK;
-      int key = key0 + row;
-      kreg[i] = (u32x4){0, 0, 0, 0};
-      if (id < BN * CK && key < L) kreg[i] = ldg16(kbase + (int64_t)key * a.k_ss + ch * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      int id = i * NT + tid;
-      int row = id / CV, ch = id - (id / CV) * CV;
-      int key = key0 + row;
-      vreg[i] = (u32x4){0, 0, 0, 0};
-      if (id < BN * CV && key < L) vreg[i] = ldg16(vbase + (int64_t)key * a.v_ss + ch * 8);
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      int id = i * NT + tid;
-      int row = id / CK, ch = id - (id / CK) * CK;
-      if (id < BN * CK)
-        *reinterpret_cast<u32x4*>(lds_k + row * DQK + ((ch ^ swz_k<CK>(row)) << 3)) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      int id = i * NT + tid;
-      int row = id / CV, ch = id - (id / CV) * CV;
-      if (id < BN * CV)
-        *reinterpret_cast<u32x4*>(lds_v + row * DV + ((ch ^ swz_v<CV>(row)) << 3)) = vreg[i];
-    }
-  };
+  if (nit > 0 && g < ntiles) issue(g, 0);
 
-  if (ntiles > 0) load_tile(0);
+  const int grp = lane >> 4;
+  const int tr_t = (lane & 15) >> 2;
+  const int tr_q = lane & 3;
 
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);
+  for (int it = 0; it < nit; ++it) {
+    const int s = it & 1;
+    const int t = it * NS + g;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this lane's DMA for stage s landed
+    __syncthreads();                      // ... and every lane's; stage s^1 is free again
+    if (it + 1 < nit && t + NS < ntiles) issue(t + NS, s ^ 1);
 
     const int key0 = t * BN;
-    if (!wave_active || key0 >= wkend) continue;   // whole tile above this wave's diagonal
+    if (t >= ntiles || !wave_active || key0 >= wkend) continue;
+    const uint16_t* kt = lds16 + (g * 2 + s) * STAGE;
+    const uint16_t* vt = kt + KT;
 
-    // ---- S^T for the two 32-key blocks
-    f32x16 sc[2];
-    bool blk_on[2];
+    // ---- S^T = K Q^T for two 32-key blocks
+    f32x16 sc[RB][NKB];
+    bool blk_on[NKB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
       blk_on[kb] = key0 + kb * 32 < wkend;
-      sc[kb] = (f32x16){};
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) sc[rb][kb] = (f32x16){};
       if (blk_on[kb]) {
         const int krow = kb * 32 + key_perm(lane & 31);
-        const uint16_t* kr = lds_k + krow * DQK;
+        const uint16_t* kr = kt + krow * DQK;
         const int sw = swz_k<CK>(krow);
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          u32x4 af = *reinterpret_cast<const u32x4*>(kr + (((2 * s + hh) ^ sw) << 3));
-          sc[kb] = T::mfma32(af, qf[s], sc[kb]);
+        for (int st = 0; st < KSTEPS; ++st) {
+          const u32x4 af = *reinterpret_cast<const u32x4*>(kr + (((2 * st + hh) ^ sw) << 3));
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) sc[rb][kb] = T::mfma32(af, qf[rb][st], sc[rb][kb]);
         }
       }
     }
 
-    // ---- scale, mask, row max
-    const bool need_mask = (key0 + BN > L) || (CAUSAL && key0 + BN - 1 > pmin);
-    float mx = -__builtin_inff();
+    // ---- mask, row max, lazy rescale, P
+    const bool need_mask = (key0 + BN > L) || (CAUSAL && key0 + BN - 1 > pmin) || !blk_on[NKB - 1];
+    u32x4 pf[RB][NKB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int rb = 0; rb < RB; ++rb) {
+      const int qpos = off + wr0 + rb * 32 + (lane & 31);
+      if (!FASTC) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sc[kb][r] * c;
-        if (need_mask) {
-          int key = key0 + kb * 32 + 16 * (r >> 3) + 8 * hh + (r & 7);
-          bool ok = blk_on[kb] && key < L && (!CAUSAL || key <= qpos);
-          x = ok ? x : -__builtin_inff();
-        } else if (!blk_on[kb]) {
-          x = -__builtin_inff();
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[rb][kb][r] *= cpre;
+      }
+      if (need_mask) {
+        asm volatile("" ::: "memory");   // keep this a branch: only edge tiles pay for masking
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + kb * 32 + 16 * (r >> 3) + 8 * hh + (r & 7);
+            const bool ok = blk_on[kb] && key < L && (!CAUSAL || key <= qpos);
+            sc[rb][kb][r] = ok ? sc[rb][kb][r] : -__builtin_inff();
+          }
+      }
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[rb][kb][r]);
+      mx = xhalf_max(mx) * c;                   // log2 units
+      const bool grow = mx > m_use[rb] + kLazyRescale;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        asm volatile("" ::: "memory");   // rare: keep the O rescale out of the common path
+        const float alpha = grow ? fast_exp2(m_use[rb] - mx) : 1.f;
+        if (grow) m_use[rb] = mx;
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < DVB; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[rb][i][r] *= alpha;
+      }
+      const float msub = (m_use[rb] == -__builtin_inff()) ? 0.f : m_use[rb];
+      float lsum = l_run[rb];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(sc[rb][kb][r], c, -msub));
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          u32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = pack_p<T>(p[8 * t2 + 2 * e], p[8 * t2 + 2 * e + 1]);
+            lsum = dot2_sum<T>(v[e], lsum);
+          }
+          pf[rb][kb][t2] = v;
         }
-        sc[kb][r] = x;
-        mx = fmaxf(mx, x);
       }
-    }
-    mx = xhalf_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const bool grow = m_new > m_run;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < DVB; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-    }
-    m_run = m_new;
-    const float msub = (m_new == -__builtin_inff()) ? 0.f : m_new;
-
-    // ---- P = exp2(x - m), row-sum, pack to the input type
-    u32x4 pf[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(sc[kb][r] - msub);
-        sc[kb][r] = p;
-        l_run += p;
-      }
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        pf[kb][t2] = (u32x4){T::pack2(sc[kb][8 * t2 + 0], sc[kb][8 * t2 + 1]),
-                             T::pack2(sc[kb][8 * t2 + 2], sc[kb][8 * t2 + 3]),
-                             T::pack2(sc[kb][8 * t2 + 4], sc[kb][8 * t2 + 5]),
-                             T::pack2(sc[kb][8 * t2 + 6], sc[kb][8 * t2 + 7])};
-      }
+      l_run[rb] = lsum;
     }
 
     // ---- O^T += V^T P^T
-    const int grp = lane >> 4;
-    const int tr_t = (lane & 15) >> 2;
-    const int tr_q = lane & 3;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
       if (!blk_on[kb]) continue;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
-        const int rowa = kb * 32 + 16 * t2 + 8 * hh + tr_t;   // keys for slots 0..3
-        const int rowb = rowa + 4;                              // keys for slots 4..7
+        const int rowa = kb * 32 + 16 * t2 + 8 * hh + tr_t;
+        const int rowb = rowa + 4;
 #pragma unroll
         for (int i = 0; i < DVB; ++i) {
           int col = i * 32 + 16 * (grp & 1) + 4 * tr_q;
-          const bool dead = (DV < 32) && (grp & 1);            // padding lanes of a 16-wide V
+          const bool dead = (DV < 32) && (grp & 1);
           if (dead) col = 4 * tr_q;
           const int ch = col >> 3, within = col & 7;
-          u32x2 lo = lds_read_tr16(lds_v + rowa * DV + ((ch ^ swz_v<CV>(rowa)) << 3) + within);
-          u32x2 hi = lds_read_tr16(lds_v + rowb * DV + ((ch ^ swz_v<CV>(rowb)) << 3) + within);
+          const u32x2 lo = lds_read_tr16(vt + rowa * DV + ((ch ^ swz_v<CV>(rowa)) << 3) + within);
+          const u32x2 hi = lds_read_tr16(vt + rowb * DV + ((ch ^ swz_v<CV>(rowb)) << 3) + within);
           u32x4 af = (u32x4){lo[0], lo[1], hi[0], hi[1]};
           if (dead) af = (u32x4){0, 0, 0, 0};
-          o[i] = T::mfma32(af, pf[kb][t2], o[i]);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) o[rb][i] = T::mfma32(af, pf[rb][kb][t2], o[rb][i]);
         }
       }
     }
   }
 
-  // ---- epilogue
-  const float lsum = xhalf_sum(l_run);
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  // ---- merge the key-split groups (exact log-sum-exp combination)
   __syncthreads();
-  uint16_t* lds_o = lds + w * 32 * OSTR;
+  if constexpr (NS > 1) {
+    float* mo = reinterpret_cast<float*>(smem);
+    float* mml = mo + MERGE_O;
+    if (g > 0) {
 #pragma unroll
-  for (int i = 0; i < DVB; ++i) {
+      for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-      const int dv = i * 32 + 8 * a4 + 4 * hh;
-      if (dv < DV) {
-        u32x2 pk = (u32x2){T::pack2(o[i][4 * a4 + 0] * inv, o[i][4 * a4 + 1] * inv),
-                           T::pack2(o[i][4 * a4 + 2] * inv, o[i][4 * a4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(lds_o + (lane & 31) * OSTR + dv) = pk;
+        for (int i = 0; i < DVB; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            mo[((((g - 1) * NR + rw) * RB + rb) * DVB * 16 + i * 16 + r) * 64 + lane] = o[rb][i][r];
+        mml[((((g - 1) * NR + rw) * RB + rb) * 2 + 0) * 64 + lane] = m_use[rb];
+        mml[((((g - 1) * NR + rw) * RB + rb) * 2 + 1) * 64 + lane] = l_run[rb];
       }
     }
+    __syncthreads();
+    if (g == 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float M = m_use[rb];
+        for (int gg = 1; gg < NS; ++gg)
+          M = fmaxf(M, mml[((((gg - 1) * NR + rw) * RB + rb) * 2 + 0) * 64 + lane]);
+        const float Ms = (M == -__builtin_inff()) ? 0.f : M;
+        const float a0 = fast_exp2(m_use[rb] - Ms);
+        float lt = l_run[rb] * a0;
+#pragma unroll
+        for (int i = 0; i < DVB; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[rb][i][r] *= a0;
+        for (int gg = 1; gg < NS; ++gg) {
+          const int base = ((gg - 1) * NR + rw) * RB + rb;
+          const float ag = fast_exp2(mml[(base * 2 + 0) * 64 + lane] - Ms);
+          lt += mml[(base * 2 + 1) * 64 + lane] * ag;
+#pragma unroll
+          for (int i = 0; i < DVB; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[rb][i][r] += ag * mo[(base * DVB * 16 + i * 16 + r) * 64 + lane];
+        }
+        m_use[rb] = M;
+        l_run[rb] = lt;
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (wave_active) {
-    uint16_t* obase = a.out + (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh;
-    constexpr int OCH = 32 * CV;
+
+  // ---- epilogue (group 0): O / l -> output type -> LDS -> coalesced stores
+  if (g == 0) {
+    float lsum[RB], inv[RB];
 #pragma unroll
-    for (int i = 0; i < (OCH + 63) / 64; ++i) {
-      int id = i * 64 + lane;
-      int row = id / CV, ch = id - (id / CV) * CV;
-      if (id < OCH && wr0 + row < a.Sq) {
-        u32x4 val = *reinterpret_cast<const u32x4*>(lds_o + row * OSTR + ch * 8);
-        stg16(obase + (int64_t)(wr0 + row) * a.o_ss + ch * 8, val);
-      }
+    for (int rb = 0; rb < RB; ++rb) {
+      lsum[rb] = xhalf_sum(l_run[rb]);
+      inv[rb] = lsum[rb] > 0.f ? 1.f / lsum[rb] : 0.f;
     }
-    if (a.lse && hh == 0 && qrow < a.Sq) {
-      a.lse[((int64_t)b * a.Hq + hq) * a.Sq + qrow] =
-          lsum > 0.f ? (m_run + __log2f(lsum)) * 0.69314718055994531f : -__builtin_inff();
+    uint16_t* lds_o = lds16 + rw * RW * OSTR;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < DVB; ++i)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int dv = i * 32 + 8 * a4 + 4 * hh;
+          if (dv < DV) {
+            const u32x2 pk = (u32x2){T::pack2(o[rb][i][4 * a4 + 0] * inv[rb], o[rb][i][4 * a4 + 1] * inv[rb]),
+                                     T::pack2(o[rb][i][4 * a4 + 2] * inv[rb], o[rb][i][4 * a4 + 3] * inv[rb])};
+            *reinterpret_cast<u32x2*>(lds_o + (rb * 32 + (lane & 31)) * OSTR + dv) = pk;
+          }
+        }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    if (wave_active) {
+      uint16_t* obase = a.out + (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh;
+      constexpr int OCH = RW * CV;
+#pragma unroll
+      for (int i = 0; i < (OCH + 63) / 64; ++i) {
+        const int id = i * 64 + lane;
+        const int row = id / CV, ch = id - (id / CV) * CV;
+        if (id < OCH && wr0 + row < a.Sq) {
+          const u32x4 val = *reinterpret_cast<const u32x4*>(lds_o + row * OSTR + ch * 8);
+          stg16(obase + (int64_t)(wr0 + row) * a.o_ss + ch * 8, val);
+        }
+      }
+      if (a.lse && hh == 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int qrow = wr0 + rb * 32 + lane;
+          if (qrow < a.Sq)
+            a.lse[((int64_t)b * a.Hq + hq) * a.Sq + qrow] =
+                lsum[rb] > 0.f ? (m_use[rb] + __log2f(lsum[rb])) * 0.69314718055994531f
+                               : -__builtin_inff();
+        }
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------- launchers
-template <class T, int DQK, int DV, bool CAUSAL>
-static hipError_t launch_tile(const AttnArgs& a0, hipStream_t st) {
-  constexpr int NW = 4;
+template <class T, int DQK, int DV, bool CAUSAL, int RB, int NR, int NS, int BN, int MINW>
+static hipError_t launch_cfg(const AttnArgs& a0, bool fastc, hipStream_t st) {
   AttnArgs a = a0;
-  a.num_qtiles = (a.Sq + 32 * NW - 1) / (32 * NW);
+  constexpr int BM = NR * 32 * RB;
+  a.num_qtiles = (a.Sq + BM - 1) / BM;
   const int64_t units = (int64_t)a.B * a.Hq * a.num_qtiles;
   if (units <= 0) return hipSuccess;
   a.xcd_remap = (units % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, NW>), dim3((unsigned)units), dim3(64 * NW),
-                     0, st, a);
+  const dim3 grid((unsigned)units), block(64 * NR * NS);
+  if (fastc)
+    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, RB, NR, NS, BN, true, MINW>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, RB, NR, NS, BN, false, MINW>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
+// Rows per workgroup and key splits per head dimension: small problems get
+// key-split groups so that every CU runs several waves.
+template <class T, int DQK, int DV, bool CAUSAL>
+static hipError_t launch_dims(const AttnArgs& a, bool fastc, hipStream_t st) {
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
+  if constexpr (DQK <= 16) {
+    return launch_cfg<T, DQK, DV, CAUSAL, 1, 4, 1, 64, 2>(a, fastc, st);
+  } else if constexpr (DQK <= 64) {
+    if (rows <= 256 * 256) return launch_cfg<T, DQK, DV, CAUSAL, 2, 2, 4, 64, 2>(a, fastc, st);
+    return launch_cfg<T, DQK, DV, CAUSAL, 2, 2, 2, 64, 2>(a, fastc, st);
+  } else {
+    if (rows <= 256 * 256) return launch_cfg<T, DQK, DV, CAUSAL, 2, 2, 2, 32, 1>(a, fastc, st);
+    return launch_cfg<T, DQK, DV, CAUSAL, 2, 4, 1, 32, 1>(a, fastc, st);
+  }
+}
+
 template <class T, int DQK, int DV>
-static hipError_t launch_tile_c(const AttnArgs& a, bool causal, hipStream_t st) {
-  return causal ? launch_tile<T, DQK, DV, true>(a, st) : launch_tile<T, DQK, DV, false>(a, st);
+static hipError_t launch_tile_c(const AttnArgs& a, bool causal, bool fastc, hipStream_t st) {
+  return causal ? launch_dims<T, DQK, DV, true>(a, fastc, st) : launch_dims<T, DQK, DV, false>(a, fastc, st);
 }
 
 template <class T>
-static hipError_t launch_tile_t(const AttnArgs& a, int dqk, int dv, bool causal, hipStream_t st) {
-  if (dqk == 16 && dv == 16) return launch_tile_c<T, 16, 16>(a, causal, st);
-  if (dqk == 64 && dv == 64) return launch_tile_c<T, 64, 64>(a, causal, st);
-  if (dqk == 128 && dv == 128) return launch_tile_c<T, 128, 128>(a, causal, st);
-  if (dqk == 192 && dv == 128) return launch_tile_c<T, 192, 128>(a, causal, st);
+static hipError_t launch_tile_t(const AttnArgs& a, int dqk, int dv, bool causal, bool fastc, hipStream_t st) {
+  if (dqk == 16 && dv == 16) return launch_tile_c<T, 16, 16>(a, causal, fastc, st);
+  if (dqk == 64 && dv == 64) return launch_tile_c<T, 64, 64>(a, causal, fastc, st);
+  if (dqk == 128 && dv == 128) return launch_tile_c<T, 128, 128>(a, causal, fastc, st);
+  if (dqk == 192 && dv == 128) return launch_tile_c<T, 192, 128>(a, causal, fastc, st);
   return hipErrorInvalidValue;
 }
 
 hipError_t run_tile_attn(const AttnArgs& a, int dtype_bf16, int dqk, int dv, bool causal,
                          hipStream_t st) {
-  return dtype_bf16 ? launch_tile_t<BF16>(a, dqk, dv, causal, st)
-                    : launch_tile_t<F16>(a, dqk, dv, causal, st);
+  const bool fastc = a.c > 0.f;
+  return dtype_bf16 ? launch_tile_t<BF16>(a, dqk, dv, causal, fastc, st)
+                    : launch_tile_t<F16>(a, dqk, dv, causal, fastc, st);
 }
 
 }  // namespace attn
