@@ -142,28 +142,59 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
   const uint16_t* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
   const uint16_t* vbase = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
 
-  // ---- tile DMA: tile t of this group into stage s
+  // ---- tile DMA: tile t of this group into stage s.  Each lane's source row
+  // and chunk inside a tile do not depend on the tile, so their byte offsets
+  // are computed once; a tile adds a wave-uniform base.  Only the tile that
+  // crosses the key length clamps rows to the last valid one.
+  constexpr int NIK = NKB * CK / 2;                 // DMA instructions per K tile
+  constexpr int NIV = NKB * CV / 2;
+  constexpr int JK = (NIK + NR - 1) / NR;           // ... per wave
+  constexpr int JV = (NIV + NR - 1) / NR;
+  int krow_j[JK], koff_j[JK], vrow_j[JV], voff_j[JV];
+#pragma unroll
+  for (int j = 0; j < JK; ++j) {
+    const int P = (rw + j * NR) * 64 + lane;
+    const int row = P / CK, pos = P % CK;
+    krow_j[j] = row;
+    koff_j[j] = (int)((int64_t)row * a.k_ss * 2) + ((pos ^ swz_k<CK>(row)) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < JV; ++j) {
+    const int P = (rw + j * NR) * 64 + lane;
+    const int row = P / CV, pos = P % CV;
+    vrow_j[j] = row;
+    voff_j[j] = (int)((int64_t)row * a.v_ss * 2) + ((pos ^ swz_v<CV>(row)) << 4);
+  }
   auto issue = [&](int t, int s) {
     uint16_t* kd = lds16 + (g * 2 + s) * STAGE;
     uint16_t* vd = kd + KT;
     const int key0 = t * BN;
+    const char* kt0 = reinterpret_cast<const char*>(kbase + (int64_t)key0 * a.k_ss);
+    const char* vt0 = reinterpret_cast<const char*>(vbase + (int64_t)key0 * a.v_ss);
+    const bool tail = key0 + BN > L;
 #pragma unroll
-    for (int I = rw; I < NKB * CK / 2; I += NR) {
-      const int P = I * 64 + lane;
-      const int row = P / CK, pos = P - (P / CK) * CK;
-      const int ch = pos ^ swz_k<CK>(row);
-      const int key = min(key0 + row, L - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + (int64_t)key * a.k_ss + ch * 8),
-                                       (LDS_AS void*)(kd + I * 512), 16, 0, 0);
+    for (int j = 0; j < JK; ++j) {
+      const int I = rw + j * NR;
+      if (NIK % NR == 0 || I < NIK) {
+        int o = koff_j[j];
+        if (tail) {
+          const int row = min(krow_j[j], L - 1 - key0);
+          o = (int)((int64_t)row * a.k_ss * 2) + (koff_j[j] - (int)((int64_t)krow_j[j] * a.k_ss * 2));
+        }
+        __builtin_amdgcn_global_load_lds((const void*)(kt0 + o), (LDS_AS void*)(kd + I * 512), 16, 0, 0);
+      }
     }
 #pragma unroll
-    for (int I = rw; I < NKB * CV / 2; I += NR) {
-      const int P = I * 64 + lane;
-      const int row = P / CV, pos = P - (P / CV) * CV;
-      const int ch = pos ^ swz_v<CV>(row);
-      const int key = min(key0 + row, L - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(vbase + (int64_t)key * a.v_ss + ch * 8),
-                                       (LDS_AS void*)(vd + I * 512), 16, 0, 0);
+    for (int j = 0; j < JV; ++j) {
+      const int I = rw + j * NR;
+      if (NIV % NR == 0 || I < NIV) {
+        int o = voff_j[j];
+        if (tail) {
+          const int row = min(vrow_j[j], L - 1 - key0);
+          o = (int)((int64_t)row * a.v_ss * 2) + (voff_j[j] - (int)((int64_t)vrow_j[j] * a.v_ss * 2));
+        }
+        __builtin_amdgcn_global_load_lds((const void*)(vt0 + o), (LDS_AS void*)(vd + I * 512), 16, 0, 0);
+      }
     }
   };
 
@@ -215,8 +246,6 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       blk_on[kb] = key0 + kb * 32 < wkend;
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) sc[rb][kb] = (f32x16){};
       if (blk_on[kb]) {
         const int krow = kb * 32 + key_perm(lane & 31);
         const uint16_t* kr = kt + krow * DQK;
@@ -225,8 +254,12 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
         for (int st = 0; st < KSTEPS; ++st) {
           const u32x4 af = *reinterpret_cast<const u32x4*>(kr + (((2 * st + hh) ^ sw) << 3));
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) sc[rb][kb] = T::mfma32(af, qf[rb][st], sc[rb][kb]);
+          for (int rb = 0; rb < RB; ++rb)
+            sc[rb][kb] = T::mfma32(af, qf[rb][st], st == 0 ? (f32x16){} : sc[rb][kb]);
         }
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) sc[rb][kb] = (f32x16){};
       }
     }
 
