@@ -109,7 +109,8 @@ KVPlan plan_kvcache(const attn_kvcache_params* p) {
     if (p->num_splits > 0) {
       len = (cap + p->num_splits - 1) / p->num_splits;
     } else {
-      const double per = (double)cap * p->B * p->Hkv / 4096.0;
+      // about 2048 splits in flight: one round of waves at 2 per SIMD
+      const double per = (double)cap * p->B * p->Hkv / 2048.0;
       len = (int)std::ceil(per);
       if (len > 2048) len = 2048;
     }

@@ -25,19 +25,26 @@
 
 namespace attn {
 
+// vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14)
+#define VMCNT_WAIT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
+
 template <class T, int DQK, int DV, bool CAUSAL>
 __global__ __launch_bounds__(64) void decode_attn_kernel(AttnArgs a) {
   constexpr int QS = (DQK + 31) / 32;          // 32-dim k-steps of S
   constexpr int CV = DV / 8;                   // chunks per V row
-  constexpr int VPL = (32 * CV + 63) / 64;     // V chunks per lane per 32-key step
+  constexpr int VPL = (32 * CV) / 64;          // V DMA instructions per 32-key step
   constexpr int DVB = DV / 16;                 // 16-wide output blocks
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[32 * DV];
+  constexpr int NK = 2 * QS;                   // K loads per lane per step
+  static_assert((32 * CV) % 64 == 0, "V step must be whole DMA instructions");
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[3 * 32 * DV];
 
   const int lane = threadIdx.x;
-  const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  // kv heads vary fastest across workgroups, so the heads of one split (whose
+  // rows share cache lines and DRAM pages) are fetched at about the same time
+  const int hkv = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
   int L, off;
   if (a.kvcache) {
-    int cb = a.seqlens ? a.seqlens[b] : a.seqlen_scalar;
+    const int cb = a.seqlens ? a.seqlens[b] : a.seqlen_scalar;
     L = cb + a.Snew;
     off = cb;
   } else {
@@ -59,33 +66,40 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(AttnArgs a) {
   u32x4 qf[QS];
 #pragma unroll
   for (int st = 0; st < QS; ++st) {
-    const int d = 32 * st + 8 * kg;
-    qf[st] = (u32x4){0, 0, 0, 0};
-    if (row_ok && d < DQK)
-      qf[st] = ldg16(a.q + (int64_t)b * a.q_sb + (int64_t)tok * a.q_ss + (int64_t)hq * a.q_sh + d);
+    const int d = min(32 * st + 8 * kg, DQK - 8);
+    const int tq = min(tok, a.Sq - 1);
+    qf[st] = ldg16(a.q + (int64_t)b * a.q_sb + (int64_t)tq * a.q_ss + (int64_t)min(hq, a.Hq - 1) * a.q_sh + d);
+    if (!row_ok || 32 * st + 8 * kg >= DQK) qf[st] = (u32x4){0, 0, 0, 0};
   }
 
   const uint16_t* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
   const uint16_t* vbase = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
 
-  auto load = [&](int kk, u32x4 (&kr)[2][QS], u32x4 (&vr)[VPL]) {
+  // One 32-key step: K straight into MFMA A operands (registers), V into an
+  // LDS stage by DMA.  Rows past the split end are fetched from its last row
+  // and masked, so every load is unconditional.
+  struct KBuf {
+    u32x4 k[2][QS];
+  };
+  auto load = [&](int kk, KBuf& B, int stage) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const int key = kk + 16 * blk + r;
+      const int key = min(kk + 16 * blk + r, k_end - 1);
 #pragma unroll
       for (int st = 0; st < QS; ++st) {
-        const int d = 32 * st + 8 * kg;
-        kr[blk][st] = (u32x4){0, 0, 0, 0};
-        if (key < k_end && d < DQK) kr[blk][st] = ldg16(kbase + (int64_t)key * a.k_ss + d);
+        const int d = min(32 * st + 8 * kg, DQK - 8);
+        B.k[blk][st] = ldg16(kbase + (int64_t)key * a.k_ss + d);
       }
     }
+    uint16_t* vd = lds_v + stage * 32 * DV;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int id = i * 64 + lane;
-      const int row = id / CV, ch = id - (id / CV) * CV;
-      const int key = kk + row;
-      vr[i] = (u32x4){0, 0, 0, 0};
-      if (id < 32 * CV && key < k_end) vr[i] = ldg16(vbase + (int64_t)key * a.v_ss + ch * 8);
+    for (int j = 0; j < VPL; ++j) {
+      const int P = j * 64 + lane;
+      const int row = P / CV, pos = P % CV;
+      const int ch = pos ^ swz_v<CV>(row);
+      const int key = min(kk + row, k_end - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(vbase + (int64_t)key * a.v_ss + ch * 8),
+                                       (LDS_AS void*)(vd + j * 512), 16, 0, 0);
     }
   };
 
@@ -96,35 +110,26 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(AttnArgs a) {
   const float c = a.c;
   const int tr_t = (lane & 15) >> 2, tr_q = lane & 3;
 
-  u32x4 kc[2][QS], vc[VPL];
-  load(k_begin, kc, vc);
-  for (int kk = k_begin; kk < k_end; kk += 32) {
-    u32x4 kn[2][QS], vn[VPL];
-    const bool more = kk + 32 < k_end;
-    if (more) load(kk + 32, kn, vn);
-
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int id = i * 64 + lane;
-      const int row = id / CV, ch = id - (id / CV) * CV;
-      if (id < 32 * CV)
-        *reinterpret_cast<u32x4*>(lds_v + row * DV + ((ch ^ swz_v<CV>(row)) << 3)) = vc[i];
-    }
-    __syncthreads();
-
+  auto step = [&](int kk, const KBuf& B, int stage, int later_steps) {
+    // this step's V DMA has landed once at most the later steps' loads are pending
+    if (later_steps >= 2) VMCNT_WAIT(2 * (NK + VPL));
+    else if (later_steps == 1) VMCNT_WAIT(NK + VPL);
+    else VMCNT_WAIT(0);
+    const uint16_t* vt = lds_v + stage * 32 * DV;
     f32x4 sa = (f32x4){0, 0, 0, 0}, sb = (f32x4){0, 0, 0, 0};
 #pragma unroll
     for (int st = 0; st < QS; ++st) {
-      sa = T::mfma16(kc[0][st], qf[st], sa);
-      sb = T::mfma16(kc[1][st], qf[st], sb);
+      u32x4 ka = B.k[0][st], kb = B.k[1][st];
+      if (32 * st + 8 * kg >= DQK) ka = kb = (u32x4){0, 0, 0, 0};
+      sa = T::mfma16(ka, qf[st], sa);
+      sb = T::mfma16(kb, qf[st], sb);
     }
     float x[8];
     float mx = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int key = kk + (i < 4 ? 4 * kg + i : 16 + 4 * kg + i - 4);
-      float v = (i < 4 ? sa[i] : sb[i - 4]) * c;
+      const float v = (i < 4 ? sa[i] : sb[i - 4]) * c;
       const bool ok = key < k_end && (!CAUSAL || key <= qpos);
       x[i] = ok ? v : -__builtin_inff();
       mx = fmaxf(mx, x[i]);
@@ -155,18 +160,30 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(AttnArgs a) {
     for (int i = 0; i < DVB; ++i) {
       const int col = i * 16 + 4 * tr_q;
       const int ch = col >> 3, within = col & 7;
-      u32x2 lo = lds_read_tr16(lds_v + rowa * DV + ((ch ^ swz_v<CV>(rowa)) << 3) + within);
-      u32x2 hi = lds_read_tr16(lds_v + rowb * DV + ((ch ^ swz_v<CV>(rowb)) << 3) + within);
+      const u32x2 lo = lds_read_tr16(vt + rowa * DV + ((ch ^ swz_v<CV>(rowa)) << 3) + within);
+      const u32x2 hi = lds_read_tr16(vt + rowb * DV + ((ch ^ swz_v<CV>(rowb)) << 3) + within);
       o[i] = T::mfma16((u32x4){lo[0], lo[1], hi[0], hi[1]}, pf, o[i]);
     }
-    if (more) {
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int st = 0; st < QS; ++st) kc[blk][st] = kn[blk][st];
-#pragma unroll
-      for (int i = 0; i < VPL; ++i) vc[i] = vn[i];
-    }
+  };
+
+  // three-deep pipeline: K registers A/B/C and LDS stages 0/1/2; two steps'
+  // loads are in flight while the current step computes
+  KBuf A, B, C;
+  load(k_begin, A, 0);
+  if (k_begin + 32 < k_end) load(k_begin + 32, B, 1);
+  for (int kk = k_begin;;) {
+    if (kk + 64 < k_end) load(kk + 64, C, 2);
+    step(kk, A, 0, (kk + 32 < k_end) + (kk + 64 < k_end));
+    kk += 32;
+    if (kk >= k_end) break;
+    if (kk + 64 < k_end) load(kk + 64, A, 0);
+    step(kk, B, 1, (kk + 32 < k_end) + (kk + 64 < k_end));
+    kk += 32;
+    if (kk >= k_end) break;
+    if (kk + 64 < k_end) load(kk + 64, B, 1);
+    step(kk, C, 2, (kk + 32 < k_end) + (kk + 64 < k_end));
+    kk += 32;
+    if (kk >= k_end) break;
   }
 
   float lt = l_run + __shfl_xor(l_run, 16);
@@ -184,18 +201,33 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(AttnArgs a) {
   }
 }
 
-// One 64-thread block per (batch, kv head, query row of that kv head).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// One wave per (batch, kv head, query row of that kv head): the splits'
+// maxima are reduced across lanes, then every lane accumulates its output
+// columns over the splits with independent (pipelined) loads.
 template <class T>
 __global__ __launch_bounds__(64) void split_merge_kernel(AttnArgs a, int DV) {
+  __shared__ float wsh[64];
   const int R = a.group * a.Sq;
   int idx = blockIdx.x;
   const int r = idx % R;
   idx /= R;
   const int hkv = idx % a.Hkv;
   const int b = idx / a.Hkv;
+  const int lane = threadIdx.x;
   int L, off;
   if (a.kvcache) {
-    int cb = a.seqlens ? a.seqlens[b] : a.seqlen_scalar;
+    const int cb = a.seqlens ? a.seqlens[b] : a.seqlen_scalar;
     L = cb + a.Snew;
     off = cb;
   } else {
@@ -209,29 +241,47 @@ __global__ __launch_bounds__(64) void split_merge_kernel(AttnArgs a, int DV) {
   const int64_t slot0 = ((int64_t)b * a.Hkv + hkv) * a.num_splits * R + r;
 
   float M = -__builtin_inff();
-  for (int s = 0; s < nvalid; ++s) M = fmaxf(M, a.ws_ml[(slot0 + (int64_t)s * R) * 2]);
-  float lsum = 0.f;
-  if (M != -__builtin_inff()) {
-    for (int s = 0; s < nvalid; ++s) {
+  for (int s = lane; s < nvalid; s += 64) M = fmaxf(M, a.ws_ml[(slot0 + (int64_t)s * R) * 2]);
+  M = wave_max(M);
+  const float Ms = (M == -__builtin_inff()) ? 0.f : M;
+  float lpart = 0.f;
+  float acc0 = 0.f, acc1 = 0.f;
+  const int dv0 = min(lane, DV - 1), dv1 = min(lane + 64, DV - 1);   // clamped: loads never branch
+  for (int s0 = 0; s0 < nvalid; s0 += 64) {
+    const int s = s0 + lane;
+    float w = 0.f;
+    if (s < nvalid) {
       const float ms = a.ws_ml[(slot0 + (int64_t)s * R) * 2];
-      const float ls = a.ws_ml[(slot0 + (int64_t)s * R) * 2 + 1];
-      if (ms != -__builtin_inff()) lsum += ls * fast_exp2(ms - M);
+      w = (ms == -__builtin_inff()) ? 0.f : fast_exp2(ms - Ms);
+      lpart += w * a.ws_ml[(slot0 + (int64_t)s * R) * 2 + 1];
     }
-  }
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  uint16_t* orow = a.out + (int64_t)b * a.o_sb + (int64_t)tok * a.o_ss + (int64_t)hq * a.o_sh;
-  for (int dv = threadIdx.x; dv < DV; dv += 64) {
-    float acc = 0.f;
-    if (lsum > 0.f) {
-      for (int s = 0; s < nvalid; ++s) {
-        const float ms = a.ws_ml[(slot0 + (int64_t)s * R) * 2];
-        if (ms == -__builtin_inff()) continue;
-        acc += a.ws_o[(slot0 + (int64_t)s * R) * DV + dv] * fast_exp2(ms - M);
+    __syncthreads();
+    wsh[lane] = w;
+    __syncthreads();
+    const int n = min(64, nvalid - s0);
+    for (int j0 = 0; j0 < n; j0 += 16) {
+      float v0[16], v1[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {   // 32 independent loads in flight per lane
+        const int sj = s0 + min(j0 + j, n - 1);
+        const float* os = a.ws_o + (slot0 + (int64_t)sj * R) * DV;
+        v0[j] = os[dv0];
+        v1[j] = os[dv1];
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float wj = (j0 + j < n) ? wsh[j0 + j] : 0.f;
+        acc0 += wj * v0[j];
+        acc1 += wj * v1[j];
       }
     }
-    orow[dv] = T::from_f32(acc * inv);
   }
-  if (a.lse && threadIdx.x == 0)
+  const float lsum = wave_sum(lpart);
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  uint16_t* orow = a.out + (int64_t)b * a.o_sb + (int64_t)tok * a.o_ss + (int64_t)hq * a.o_sh;
+  if (lane < DV) orow[lane] = T::from_f32(acc0 * inv);
+  if (lane + 64 < DV) orow[lane + 64] = T::from_f32(acc1 * inv);
+  if (a.lse && lane == 0)
     a.lse[((int64_t)b * a.Hq + hq) * a.Sq + tok] =
         lsum > 0.f ? (M + __log2f(lsum)) * 0.69314718055994531f : -__builtin_inff();
 }
@@ -240,7 +290,7 @@ __global__ __launch_bounds__(64) void split_merge_kernel(AttnArgs a, int DV) {
 template <class T, int DQK, int DV>
 static hipError_t launch_decode(const AttnArgs& a0, bool causal, hipStream_t st) {
   AttnArgs a = a0;
-  dim3 grid((unsigned)a.num_splits, (unsigned)a.Hkv, (unsigned)a.B);
+  dim3 grid((unsigned)a.Hkv, (unsigned)a.num_splits, (unsigned)a.B);
   if (causal)
     hipLaunchKernelGGL((decode_attn_kernel<T, DQK, DV, true>), grid, dim3(64), 0, st, a);
   else

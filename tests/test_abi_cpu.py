@@ -160,7 +160,7 @@ def test_kvcache_workspace_plan():
     # decode path: partials for every (batch, kv head, split, row) plus rotated q
     p, keep = _kv(B=8, Hq=32, Hkv=8, D=128, cap=8192, rotary=128)
     need = E.kvcache_workspace_size(p)
-    split = 128
+    split = 256
     nsp = 8192 // split
     R = 4
     q_rot = 8 * 1 * 32 * 128 * 2
