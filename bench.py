@@ -37,7 +37,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of workloads to time (default: all)")
+    ap.add_argument("--only", default="",
+                    help="comma list of extra workloads to time: decode, chunked, asym, empty "
+                         "(default: all; 'none' times the headline only)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize", default="",
+                    help="print a text summary of a rocprofv3 CSV output directory and exit")
     return ap.parse_args()
 
 
@@ -58,8 +64,48 @@ def time_loop(calls, steps, warmup, torch):
     return e0.elapsed_time(e1) / 1e3 / steps
 
 
+def summarize(d):
+    """Text summary of rocprofv3 CSV output: kernel durations and per-dispatch counters."""
+    import csv
+    import glob
+    from collections import defaultdict
+    for path in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        print("# kernel statistics (%s)" % os.path.relpath(path, d))
+        print("%-100s %6s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us"))
+        for r in csv.DictReader(open(path)):
+            print("%-100s %6s %12.2f %12.2f %12.2f" % (r["Name"][:100], r["Calls"],
+                  float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        print("# counters per dispatch, averaged (%s)" % os.path.relpath(path, d))
+        agg = defaultdict(lambda: defaultdict(list))
+        for r in csv.DictReader(open(path)):
+            agg[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        for k, cs in agg.items():
+            print(k[:120])
+            for cn, v in sorted(cs.items()):
+                print("    %-32s %16.6g   (dispatches: %d)" % (cn, sum(v) / len(v), len(v)))
+
+
+def traffic_entry(kernel_key):
+    """Measured HBM bytes per launch for a kernel, if its source is unchanged since measured."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel_key)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -77,7 +123,7 @@ def main():
     results = {}
 
     def want(name):
-        return not only or name in only
+        return not only or name in only   # "none" matches no workload
 
     # ---------------- headline: attn_fwd B=2 H=8 S=2048 D=64 fp16, non-causal + causal
     hl = {}
@@ -170,11 +216,21 @@ def main():
         t = time_loop([call], K, Wm, torch)
         results["kvcache_empty"] = {"us": t * 1e6}
 
+    # ---------------- plain copy (calibrates the HBM byte counters)
+    if args.copy_mib:
+        src = torch.empty(args.copy_mib * 2**20 // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        t = time_loop([lambda: dst.copy_(src)], K, Wm, torch)
+        results["copy_%dmib" % args.copy_mib] = {"us": t * 1e6, "gbs_read_plus_write":
+                                                 2 * args.copy_mib * 2**20 / t / 1e9}
+        del src, dst
+
     # ---------------- roofline entry: the non-causal headline kernel
     t_nc, fl_nc = hl[False]
     roofline = {"kernel": "tile_attn_kernel<F16,64,64,non-causal>", "bound": "mfma",
                 "achieved": fl_nc / t_nc / 1e12, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": fl_nc / t_nc / 1e12 / PEAK_TFLOPS, "traffic": None,
+                "frac": fl_nc / t_nc / 1e12 / PEAK_TFLOPS,
+                "traffic": traffic_entry("tile_attn_fwd_b2h8s2048d64"),
                 "avg_launch_us": t_nc * 1e6,
                 "algorithmic": "2*(64+64) flop x 2*8*2048*2048 (query,key) pairs = %.4g GFLOP per launch"
                                % (fl_nc / 1e9)}
