@@ -73,7 +73,8 @@ __device__ __forceinline__ float dot2_sum<BF16>(uint32_t p, float acc) {
                                          (bf16x2){(__bf16)1.f, (__bf16)1.f}, acc, false);
 }
 
-template <class T, int DQK, int DV, bool CAUSAL, int RB, int NR, int NS, int BN, bool FASTC, int MINW>
+template <class T, int DQK, int DV, bool CAUSAL, int RB, int NR, int NS, int BN, bool PAIR, bool FASTC,
+          int MINW>
 __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs a) {
   constexpr int NKB = BN / 32;                           // 32-key MFMA blocks per tile
   constexpr int RW = 32 * RB;
@@ -107,13 +108,19 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
     const int per = gridDim.x >> 3;
     u = (u & 7) * per + (u >> 3);
   }
+  // PAIR (causal): a unit is the query-tile pair (nqt-1-p, p), processed one
+  // after the other, so every workgroup gets the same number of key tiles.
   const int nqt = a.num_qtiles;
-  const int bh = u / nqt;
-  int qt = u - bh * nqt;
-  if (CAUSAL) qt = nqt - 1 - qt;
+  const int nub = PAIR ? (nqt + 1) / 2 : nqt;   // units per (batch, head)
+  const int bh = u / nub;
+  const int pu = u - bh * nub;
   const int b = bh / a.Hq;
   const int hq = bh - b * a.Hq;
   const int hkv = hq / a.group;
+  const int nslots = (PAIR && nqt - 1 - pu != pu) ? 2 : 1;
+  for (int slot = 0; slot < nslots; ++slot) {
+  int qt = pu;
+  if (CAUSAL) qt = (PAIR && slot == 1) ? pu : nqt - 1 - pu;   // heavy tiles first
 
   int L, off;
   if (a.kvcache) {
@@ -444,22 +451,26 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
       }
     }
   }
+  __syncthreads();   // the staging tile is reused by the next slot
+  }   // slot
 }
 
 // ---------------------------------------------------------------- launchers
-template <class T, int DQK, int DV, bool CAUSAL, int RB, int NR, int NS, int BN, int MINW>
+template <class T, int DQK, int DV, bool CAUSAL, int RB, int NR, int NS, int BN, bool PAIR, int MINW>
 static hipError_t launch_cfg(const AttnArgs& a0, bool fastc, hipStream_t st) {
   AttnArgs a = a0;
   constexpr int BM = NR * 32 * RB;
   a.num_qtiles = (a.Sq + BM - 1) / BM;
-  const int64_t units = (int64_t)a.B * a.Hq * a.num_qtiles;
+  const int64_t units = (int64_t)a.B * a.Hq * (PAIR ? (a.num_qtiles + 1) / 2 : a.num_qtiles);
   if (units <= 0) return hipSuccess;
   a.xcd_remap = (units % 8 == 0) ? 1 : 0;
   const dim3 grid((unsigned)units), block(64 * NR * NS);
   if (fastc)
-    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, RB, NR, NS, BN, true, MINW>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, RB, NR, NS, BN, PAIR, true, MINW>), grid, block,
+                       0, st, a);
   else
-    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, RB, NR, NS, BN, false, MINW>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, RB, NR, NS, BN, PAIR, false, MINW>), grid, block,
+                       0, st, a);
   return hipGetLastError();
 }
 
@@ -469,13 +480,14 @@ template <class T, int DQK, int DV, bool CAUSAL>
 static hipError_t launch_dims(const AttnArgs& a, bool fastc, hipStream_t st) {
   const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
   if constexpr (DQK <= 16) {
-    return launch_cfg<T, DQK, DV, CAUSAL, 1, 4, 1, 64, 2>(a, fastc, st);
+    return launch_cfg<T, DQK, DV, CAUSAL, 1, 4, 1, 64, false, 2>(a, fastc, st);
   } else if constexpr (DQK <= 64) {
-    if (rows <= 256 * 256) return launch_cfg<T, DQK, DV, CAUSAL, 2, 2, 4, 64, 2>(a, fastc, st);
-    return launch_cfg<T, DQK, DV, CAUSAL, 2, 2, 2, 64, 2>(a, fastc, st);
+    if (CAUSAL) return launch_cfg<T, DQK, DV, CAUSAL, 1, 2, 4, 64, true, 2>(a, fastc, st);
+    if (rows <= 256 * 256) return launch_cfg<T, DQK, DV, CAUSAL, 2, 2, 4, 64, false, 2>(a, fastc, st);
+    return launch_cfg<T, DQK, DV, CAUSAL, 2, 2, 2, 64, false, 2>(a, fastc, st);
   } else {
-    if (rows <= 256 * 256) return launch_cfg<T, DQK, DV, CAUSAL, 2, 2, 2, 32, 1>(a, fastc, st);
-    return launch_cfg<T, DQK, DV, CAUSAL, 2, 4, 1, 32, 1>(a, fastc, st);
+    if (rows <= 256 * 256) return launch_cfg<T, DQK, DV, CAUSAL, 2, 2, 2, 32, false, 1>(a, fastc, st);
+    return launch_cfg<T, DQK, DV, CAUSAL, 2, 4, 1, 32, false, 1>(a, fastc, st);
   }
 }
 
