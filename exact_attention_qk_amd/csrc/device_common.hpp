@@ -30,6 +30,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -106,6 +107,23 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Buffer resource over [base, base + bytes) for raw (unswizzled, stride 0)
+// loads: offsets at or past `bytes` read as zero, per dword.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return (i32x4){(int)(uint32_t)p, (int)((uint32_t)(p >> 32) & 0xFFFFu), bytes, 0x00020000};
+}
+
+// 16 bytes per lane from a buffer resource (byte offset voff) into LDS at
+// lds_addr + 16 * lane.  The instruction has no destination register; the
+// caller waits for completion with vmcnt before the LDS data is read.
+__device__ __forceinline__ void dma_b128(i32x4 rsrc, uint32_t lds_addr, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
 
 // 16-byte chunk swizzles of row-major LDS tiles.  A tile row of D 16-bit
 // elements holds C = D/8 chunks; chunk c of row r is stored at position

@@ -17,8 +17,8 @@
 //  * each group double-buffers its 64-key K/V tiles in LDS with direct
 //    global->LDS loads (global_load_lds_dwordx4): the next tile streams in
 //    while the current one is consumed, without staging registers.  Rows past
-//    the key length are fetched from the last valid row (so stale or NaN cache
-//    content is never read) and masked;
+//    the key length are outside the tile's buffer resource and read as zero
+//    (stale or NaN cache content is never read); their scores are masked;
 //  * S^T = K Q^T on v_mfma_f32_32x32x16: one K fragment read from LDS feeds RB
 //    MFMAs, and a lane owns one query row, so the row max needs one lane^32
 //    exchange and the row sum none until the end;
@@ -94,6 +94,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
   constexpr int LDS_BYTES = cmax(LDS_KV, cmax(MERGE_B, LDS_O));
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
   uint16_t* lds16 = reinterpret_cast<uint16_t*>(smem);
+  const uint32_t smem_addr = (uint32_t)reinterpret_cast<uintptr_t>((LDS_AS void*)smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -151,57 +152,44 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
 
   // ---- tile DMA: tile t of this group into stage s.  Each lane's source row
   // and chunk inside a tile do not depend on the tile, so their byte offsets
-  // are computed once; a tile adds a wave-uniform base.  Only the tile that
-  // crosses the key length clamps rows to the last valid one.
+  // are computed once.  A tile is read through a buffer resource that starts
+  // at its first key row and ends after its last valid one: rows past the key
+  // length read as zero (and are masked), without per-lane clamping.
   constexpr int NIK = NKB * CK / 2;                 // DMA instructions per K tile
   constexpr int NIV = NKB * CV / 2;
   constexpr int JK = (NIK + NR - 1) / NR;           // ... per wave
   constexpr int JV = (NIV + NR - 1) / NR;
-  int krow_j[JK], koff_j[JK], vrow_j[JV], voff_j[JV];
+  int koff_j[JK], voff_j[JV];
 #pragma unroll
   for (int j = 0; j < JK; ++j) {
     const int P = (rw + j * NR) * 64 + lane;
     const int row = P / CK, pos = P % CK;
-    krow_j[j] = row;
-    koff_j[j] = (int)((int64_t)row * a.k_ss * 2) + ((pos ^ swz_k<CK>(row)) << 4);
+    koff_j[j] = row * a.k_ss * 2 + ((pos ^ swz_k<CK>(row)) << 4);
   }
 #pragma unroll
   for (int j = 0; j < JV; ++j) {
     const int P = (rw + j * NR) * 64 + lane;
     const int row = P / CV, pos = P % CV;
-    vrow_j[j] = row;
-    voff_j[j] = (int)((int64_t)row * a.v_ss * 2) + ((pos ^ swz_v<CV>(row)) << 4);
+    voff_j[j] = row * a.v_ss * 2 + ((pos ^ swz_v<CV>(row)) << 4);
   }
   auto issue = [&](int t, int s) {
-    uint16_t* kd = lds16 + (g * 2 + s) * STAGE;
-    uint16_t* vd = kd + KT;
+    const uint32_t kd = smem_addr + (uint32_t)((g * 2 + s) * STAGE) * 2;
+    const uint32_t vd = kd + KT * 2;
     const int key0 = t * BN;
-    const char* kt0 = reinterpret_cast<const char*>(kbase + (int64_t)key0 * a.k_ss);
-    const char* vt0 = reinterpret_cast<const char*>(vbase + (int64_t)key0 * a.v_ss);
-    const bool tail = key0 + BN > L;
+    const int rows = min(BN, L - key0);
+    const i32x4 rk = make_rsrc(kbase + (int64_t)key0 * a.k_ss, rows * a.k_ss * 2);
+    const i32x4 rv = make_rsrc(vbase + (int64_t)key0 * a.v_ss, rows * a.v_ss * 2);
 #pragma unroll
     for (int j = 0; j < JK; ++j) {
       const int I = rw + j * NR;
-      if (NIK % NR == 0 || I < NIK) {
-        int o = koff_j[j];
-        if (tail) {
-          const int row = min(krow_j[j], L - 1 - key0);
-          o = (int)((int64_t)row * a.k_ss * 2) + (koff_j[j] - (int)((int64_t)krow_j[j] * a.k_ss * 2));
-        }
-        __builtin_amdgcn_global_load_lds((const void*)(kt0 + o), (LDS_AS void*)(kd + I * 512), 16, 0, 0);
-      }
+      if (NIK % NR == 0 || I < NIK)
+        dma_b128(rk, kd + I * 1024, koff_j[j]);
     }
 #pragma unroll
     for (int j = 0; j < JV; ++j) {
       const int I = rw + j * NR;
-      if (NIV % NR == 0 || I < NIV) {
-        int o = voff_j[j];
-        if (tail) {
-          const int row = min(vrow_j[j], L - 1 - key0);
-          o = (int)((int64_t)row * a.v_ss * 2) + (voff_j[j] - (int)((int64_t)vrow_j[j] * a.v_ss * 2));
-        }
-        __builtin_amdgcn_global_load_lds((const void*)(vt0 + o), (LDS_AS void*)(vd + I * 512), 16, 0, 0);
-      }
+      if (NIV % NR == 0 || I < NIV)
+        dma_b128(rv, vd + I * 1024, voff_j[j]);
     }
   };
 
