@@ -470,12 +470,12 @@ static hipError_t launch_dims(const AttnArgs& a, bool fastc, hipStream_t st) {
   if constexpr (DQK <= 16) {
     return launch_cfg<T, DQK, DV, CAUSAL, 1, 4, 1, 64, false, 2>(a, fastc, st);
   } else if constexpr (DQK <= 64) {
-    if (CAUSAL) return launch_cfg<T, DQK, DV, CAUSAL, 1, 2, 4, 64, true, 2>(a, fastc, st);
-    if (rows <= 256 * 256) return launch_cfg<T, DQK, DV, CAUSAL, 2, 2, 4, 64, false, 2>(a, fastc, st);
+    if (CAUSAL) return launch_cfg<T, DQK, DV, CAUSAL, 1, 2, 4, 32, true, 2>(a, fastc, st);
+    if (rows <= 256 * 256) return launch_cfg<T, DQK, DV, CAUSAL, 1, 4, 2, 64, false, 2>(a, fastc, st);
     return launch_cfg<T, DQK, DV, CAUSAL, 2, 2, 2, 64, false, 2>(a, fastc, st);
   } else {
-    if (rows <= 256 * 256) return launch_cfg<T, DQK, DV, CAUSAL, 2, 2, 2, 32, false, 1>(a, fastc, st);
-    return launch_cfg<T, DQK, DV, CAUSAL, 2, 4, 1, 32, false, 1>(a, fastc, st);
+    // one query block per wave keeps two waves per SIMD at these head sizes
+    return launch_cfg<T, DQK, DV, CAUSAL, 1, 4, 1, 64, false, 2>(a, fastc, st);
   }
 }
 
