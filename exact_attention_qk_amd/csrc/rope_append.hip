@@ -10,7 +10,12 @@
 // 16-bit inputs are exact in fp32, so the result is the exact value rounded
 // once -- and then rounded to the storage type (round to nearest even).
 //
-// One wave per row; a lane owns whole pairs, so rotating in place is safe.
+// Vector path (rd a multiple of 16, 16-byte aligned tables): a lane owns 8
+// consecutive elements (16 bytes) of a row and a wave holds 64 / (D/8) rows.
+// Interleaved pairs lie inside a lane's chunk; for the half-split layout a
+// lane also reads its partner chunk (rd/2 elements away) before any lane of
+// the row stores, so rotating in place is safe.  Other rotary widths use one
+// wave per row, a lane owning whole pairs.
 // The KV-cache append runs three row sets in one launch (blockIdx.y):
 // new keys (rotated, written to cache rows c_b + i), new values (copied to
 // cache rows c_b + i) and, with rotary tables, the queries (rotated into a
@@ -59,6 +64,85 @@ __device__ __forceinline__ void process_row(const RowSet& rs, int row, int lane)
   for (int d = a.rd + lane; d < a.D; d += 64) y[d] = x[d];
 }
 
+// y for one 16-bit element: first half of a pair -> x1*c - x2*s, second -> x1*s + x2*c
+template <class T>
+__device__ __forceinline__ uint16_t rot_one(uint16_t x1b, uint16_t x2b, uint16_t cb, uint16_t sb, bool second,
+                                            bool conj) {
+  const float x1 = T::to_f32(x1b), x2 = T::to_f32(x2b), c = T::to_f32(cb);
+  float sn = T::to_f32(sb);
+  if (conj) sn = -sn;
+  float y = second ? x1 * sn + x2 * c : x1 * c - x2 * sn;
+  asm volatile("" : "+v"(y));   // round the exact value to fp32 first (see process_row)
+  return T::from_f32(y);
+}
+
+template <class T>
+__global__ __launch_bounds__(256) void rope_vec_kernel(RowSet s0, RowSet s1, RowSet s2) {
+  const RowSet& rs = blockIdx.y == 0 ? s0 : (blockIdx.y == 1 ? s1 : s2);
+  const RopeArgs& a = rs.t;
+  const int lpr = a.D >> 3;                 // lanes per row
+  const int rpw = 64 / lpr;                 // rows per wave
+  const int lane = threadIdx.x & 63;
+  const int sub = lane / lpr;
+  const int c = lane - sub * lpr;           // 16-byte chunk of the row
+  if (sub >= rpw) return;
+  const int row = (blockIdx.x * 4 + (threadIdx.x >> 6)) * rpw + sub;
+  const int total = a.B * a.S * a.H;
+  if (row >= total) return;
+  const int h = row % a.H;
+  const int bs = row / a.H;
+  const int s = bs % a.S;
+  const int b = bs / a.S;
+  const int off = a.offsets ? a.offsets[b] : a.offset_scalar;
+  const int ds = rs.dst_at_offset ? off + s : s;
+  const uint16_t* x = a.x + (int64_t)b * a.x_sb + (int64_t)s * a.x_ss + (int64_t)h * a.x_sh;
+  uint16_t* y = a.y + (int64_t)b * a.y_sb + (int64_t)ds * a.y_ss + (int64_t)h * a.y_sh;
+  const int d0 = c * 8;
+  const u32x4 xv = ldg16(x + d0);
+  if (a.copy_only || d0 >= a.rd) {
+    stg16(y + d0, xv);
+    return;
+  }
+  const int half = a.rd >> 1;
+  const int64_t pos = off + s;
+  u32x4 out;
+  if (a.interleaved) {
+    // elements 2e, 2e+1 of the chunk form pair d0/2 + e
+    const u32x2 cc = *reinterpret_cast<const u32x2*>(a.cos + pos * half + (d0 >> 1));
+    const u32x2 sv = *reinterpret_cast<const u32x2*>(a.sin + pos * half + (d0 >> 1));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint16_t x1 = (uint16_t)(xv[e] & 0xFFFFu), x2 = (uint16_t)(xv[e] >> 16);
+      const uint32_t cw = cc[e >> 1], sw = sv[e >> 1];
+      const uint16_t cb = (uint16_t)((e & 1) ? cw >> 16 : cw & 0xFFFFu);
+      const uint16_t sb = (uint16_t)((e & 1) ? sw >> 16 : sw & 0xFFFFu);
+      const uint16_t y1 = rot_one<T>(x1, x2, cb, sb, false, a.conjugate);
+      const uint16_t y2 = rot_one<T>(x1, x2, cb, sb, true, a.conjugate);
+      out[e] = (uint32_t)y1 | ((uint32_t)y2 << 16);
+    }
+  } else {
+    const bool second = d0 >= half;
+    const int j0 = second ? d0 - half : d0;
+    const u32x4 pv = ldg16(x + (second ? d0 - half : d0 + half));
+    const u32x4 cc = ldg16(a.cos + pos * half + j0);
+    const u32x4 sv = ldg16(a.sin + pos * half + j0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t own = (uint16_t)(xv[e >> 1] >> (16 * (e & 1)));
+      const uint16_t oth = (uint16_t)(pv[e >> 1] >> (16 * (e & 1)));
+      const uint16_t cb = (uint16_t)(cc[e >> 1] >> (16 * (e & 1)));
+      const uint16_t sb = (uint16_t)(sv[e >> 1] >> (16 * (e & 1)));
+      const uint16_t r = second ? rot_one<T>(oth, own, cb, sb, true, a.conjugate)
+                                : rot_one<T>(own, oth, cb, sb, false, a.conjugate);
+      if (e & 1)
+        out[e >> 1] |= (uint32_t)r << 16;
+      else
+        out[e >> 1] = r;
+    }
+  }
+  stg16(y + d0, out);
+}
+
 template <class T>
 __global__ __launch_bounds__(256) void rope_rows_kernel(RowSet s0, RowSet s1, RowSet s2) {
   const RowSet& rs = blockIdx.y == 0 ? s0 : (blockIdx.y == 1 ? s1 : s2);
@@ -68,15 +152,39 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(RowSet s0, RowSet s1, Ro
   process_row<T>(rs, row, threadIdx.x & 63);
 }
 
+static bool vec_ok(const RowSet& r) {
+  const RopeArgs& a = r.t;
+  if (a.D % 8 != 0 || a.D > 512) return false;
+  if (a.copy_only || a.rd == 0) return true;
+  if (a.rd % 16 != 0) return false;
+  return (reinterpret_cast<uintptr_t>(a.cos) % 16 == 0) && (reinterpret_cast<uintptr_t>(a.sin) % 16 == 0);
+}
+
 hipError_t run_rope_rows(const RowSet* sets, int nsets, int dtype_bf16, hipStream_t st) {
   if (nsets <= 0) return hipSuccess;
   RowSet s[3] = {sets[0], nsets > 1 ? sets[1] : sets[0], nsets > 2 ? sets[2] : sets[0]};
   int64_t maxrows = 0;
+  bool vec = true;
+  int64_t vec_blocks = 0;
   for (int i = 0; i < nsets; ++i) {
-    int64_t n = (int64_t)sets[i].t.B * sets[i].t.S * sets[i].t.H;
+    const int64_t n = (int64_t)sets[i].t.B * sets[i].t.S * sets[i].t.H;
     if (n > maxrows) maxrows = n;
+    vec = vec && vec_ok(sets[i]);
+    if (vec) {
+      const int rpw = 64 / (sets[i].t.D / 8);
+      const int64_t blocks = (n + 4 * rpw - 1) / (4 * rpw);
+      if (blocks > vec_blocks) vec_blocks = blocks;
+    }
   }
   if (maxrows == 0) return hipSuccess;
+  if (vec) {
+    const dim3 grid((unsigned)vec_blocks, (unsigned)nsets);
+    if (dtype_bf16)
+      hipLaunchKernelGGL(rope_vec_kernel<BF16>, grid, dim3(256), 0, st, s[0], s[1], s[2]);
+    else
+      hipLaunchKernelGGL(rope_vec_kernel<F16>, grid, dim3(256), 0, st, s[0], s[1], s[2]);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((maxrows + 3) / 4), (unsigned)nsets);
   if (dtype_bf16)
     hipLaunchKernelGGL(rope_rows_kernel<BF16>, grid, dim3(256), 0, st, s[0], s[1], s[2]);

@@ -330,11 +330,13 @@ def test_kvcache_fused_rope_equals_unfused():
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("interleaved", [False, True])
-@pytest.mark.parametrize("rd", [32, 128])
-def test_rope_apply_bit_exact(dtype, interleaved, rd):
+@pytest.mark.parametrize("D,rd", [(128, 32), (128, 40), (128, 128), (192, 96), (16, 16), (64, 48)])
+def test_rope_apply_bit_exact(dtype, interleaved, D, rd):
+    # rd % 16 == 0 takes the 16-byte-per-lane path (several rows per wave for
+    # D < 512); rd = 40 takes the per-pair path
     tdt = W.DTYPES[dtype]
-    g = torch.Generator().manual_seed(rd + interleaved)
-    x = torch.randn(3, 50, 4, 128, generator=g).to(tdt)
+    g = torch.Generator().manual_seed(rd + interleaved + D)
+    x = torch.randn(3, 50, 4, D, generator=g).to(tdt)
     cos, sin = W.rope_tables(512, rd, 10000.0, tdt)
     offs = torch.tensor([0, 17, 400], dtype=torch.int32)
     mod = E()
