@@ -198,7 +198,7 @@ def attn_fwd_kvcache(q, k_cache, v_cache, k=None, v=None, rotary_cos=None, rotar
     p = kvcache_params(q, k_cache, v_cache, k, v, rotary_cos, rotary_sin, cache_seqlens, causal,
                        softmax_scale, bool(rotary_interleaved), out, lse, None, num_splits)
     need = kvcache_workspace_size(p)
-    if workspace is None or workspace.numel() < need:
+    if workspace is None or workspace.numel() < need + 256:
         workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
     off = (-workspace.data_ptr()) % 256
     ws = workspace[off:]

@@ -88,9 +88,12 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct KVPlan {
   bool rotary = false;
   bool decode = false;      // split-KV path (few query rows per kv head)
+  bool fused = false;       // decode kernel also appends the new rows and applies the rotary embedding
   int split_len = 0, num_splits = 0;
   size_t off_qrot = 0, off_o = 0, off_ml = 0, total = 0;
 };
+
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
 KVPlan plan_kvcache(const attn_kvcache_params* p) {
   KVPlan k;
@@ -98,8 +101,10 @@ KVPlan plan_kvcache(const attn_kvcache_params* p) {
   const int group = p->Hq / p->Hkv;
   const int R = group * p->Sq;
   k.decode = R <= 16;
+  k.fused = k.decode && (!k.rotary || (p->rotary_dim % 16 == 0 && aligned16(p->rotary_cos) &&
+                                       aligned16(p->rotary_sin)));
   size_t off = 0;
-  if (k.rotary) {
+  if (k.rotary && !k.fused) {
     k.off_qrot = off;
     off = align_up(off + (size_t)p->B * p->Sq * p->Hq * p->Dqk * 2);
   }
@@ -297,10 +302,11 @@ int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream) {
   }
 
   char* ws = static_cast<char*>(p->workspace);
-  uint16_t* qrot = plan.rotary ? reinterpret_cast<uint16_t*>(ws + plan.off_qrot) : nullptr;
+  uint16_t* qrot = (plan.rotary && !plan.fused) ? reinterpret_cast<uint16_t*>(ws + plan.off_qrot) : nullptr;
   const int64_t qr_sh = p->Dqk, qr_ss = (int64_t)p->Hq * p->Dqk, qr_sb = (int64_t)p->Sq * qr_ss;
 
-  // 1. append new rows (rotating keys) and rotate the queries
+  // 1. append new rows (rotating keys) and rotate the queries, unless the
+  //    decode kernel does both itself
   attn::RowSet sets[3];
   int ns = 0;
   auto rowset = [&](const attn_tensor4& x, const uint16_t* ydata, int64_t ysb, int64_t yss,
@@ -323,13 +329,15 @@ int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream) {
     r.dst_at_offset = at_offset ? 1 : 0;
     sets[ns++] = r;
   };
-  if (p->Snew > 0) {
-    rowset(p->k_new, static_cast<uint16_t*>(p->k_cache.data), p->k_cache.stride_b, p->k_cache.stride_s,
-           p->k_cache.stride_h, p->Snew, p->Hkv, p->Dqk, plan.rotary, true);
-    rowset(p->v_new, static_cast<uint16_t*>(p->v_cache.data), p->v_cache.stride_b, p->v_cache.stride_s,
-           p->v_cache.stride_h, p->Snew, p->Hkv, p->Dv, false, true);
+  if (!plan.fused) {
+    if (p->Snew > 0) {
+      rowset(p->k_new, static_cast<uint16_t*>(p->k_cache.data), p->k_cache.stride_b, p->k_cache.stride_s,
+             p->k_cache.stride_h, p->Snew, p->Hkv, p->Dqk, plan.rotary, true);
+      rowset(p->v_new, static_cast<uint16_t*>(p->v_cache.data), p->v_cache.stride_b, p->v_cache.stride_s,
+             p->v_cache.stride_h, p->Snew, p->Hkv, p->Dv, false, true);
+    }
+    if (plan.rotary) rowset(p->q, qrot, qr_sb, qr_ss, qr_sh, p->Sq, p->Hq, p->Dqk, true, false);
   }
-  if (plan.rotary) rowset(p->q, qrot, qr_sb, qr_ss, qr_sh, p->Sq, p->Hq, p->Dqk, true, false);
   if (ns > 0) {
     hipError_t he = attn::run_rope_rows(sets, ns, bf16, st);
     if (he != hipSuccess) return hip_fail(he, "kvcache append launch");
@@ -337,7 +345,7 @@ int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream) {
 
   // 2. attention over the cache prefix
   attn::AttnArgs a = base_args();
-  if (plan.rotary) {
+  if (qrot) {
     a.q = qrot; a.q_sb = qr_sb; a.q_ss = qr_ss; a.q_sh = qr_sh;
   } else {
     set_q(a, p->q);
@@ -357,6 +365,21 @@ int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream) {
     a.num_splits = plan.num_splits;
     a.ws_o = reinterpret_cast<float*>(ws + plan.off_o);
     a.ws_ml = reinterpret_cast<float*>(ws + plan.off_ml);
+    if (plan.fused) {
+      a.fused = 1;
+      if (p->Snew > 0) {
+        a.kn = static_cast<const uint16_t*>(p->k_new.data);
+        a.kn_sb = p->k_new.stride_b; a.kn_ss = p->k_new.stride_s; a.kn_sh = p->k_new.stride_h;
+        a.vn = static_cast<const uint16_t*>(p->v_new.data);
+        a.vn_sb = p->v_new.stride_b; a.vn_ss = p->v_new.stride_s; a.vn_sh = p->v_new.stride_h;
+      }
+      if (plan.rotary) {
+        a.rcos = static_cast<const uint16_t*>(p->rotary_cos);
+        a.rsin = static_cast<const uint16_t*>(p->rotary_sin);
+        a.rd = p->rotary_dim;
+        a.rinter = p->rotary_interleaved ? 1 : 0;
+      }
+    }
     he = attn::run_decode_attn(a, bf16, p->Dqk, p->Dv, p->causal != 0, st);
   } else {
     he = attn::run_tile_attn(a, bf16, p->Dqk, p->Dv, p->causal != 0, st);

@@ -23,6 +23,12 @@ struct AttnArgs {
   int split_len, num_splits;
   float* ws_o;                // [B, Hkv, num_splits, R, Dv] fp32 partial numerators
   float* ws_ml;               // [B, Hkv, num_splits, R, 2]  running max (log2 units), sum
+  // decode with the append and the rotary embedding done in the same kernel
+  int fused;                  // 1: keys >= c_b come from kn/vn (rotated) and are written to the cache
+  const uint16_t* kn; int64_t kn_sb, kn_ss, kn_sh;
+  const uint16_t* vn; int64_t vn_sb, vn_ss, vn_sh;
+  const uint16_t* rcos; const uint16_t* rsin;   // [*, rd/2] tables, rows 16-byte aligned
+  int rd, rinter;             // rotary width (0: none, else a multiple of 16), interleaved pairs
 };
 
 struct RopeArgs {

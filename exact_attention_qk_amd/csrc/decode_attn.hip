@@ -1,24 +1,31 @@
 // Split-KV attention for few query rows per kv head (single-token decode and
-// short appends), plus the log-sum-exp merge of the splits.
+// short appends), and the log-sum-exp merge of the splits.
 //
 // Method: the decode-time variant of exact attention (flash-attention issue
 // #1402, flash_attn_with_kvcache): queries attend the cache prefix of their
 // batch.  With one new token per step there are only (Hq/Hkv) * Sq query rows
 // per kv head, so the key range of each (batch, kv head) is cut into splits
 // that run in parallel; each split keeps its own running max, sum and
-// unnormalised output, and a second kernel combines the splits exactly:
+// unnormalised output, and a second kernel combines them exactly:
 //   M = max_s m_s,  l = sum_s l_s 2^(m_s - M),  O = sum_s O_s 2^(m_s - M) / l.
+// A (batch, kv head) whose keys fit in one split writes its output directly.
 //
-// One wave per (split, kv head, batch).  The R <= 16 query rows of a kv head
+// Fused append (when the rotary width is 0 or a multiple of 16): queries are
+// rotated as they are loaded; the split whose key range holds the new
+// positions [c_b, c_b + Snew) writes the rotated new keys (same rounding as
+// rope_apply) and the new values into the cache before it streams its keys,
+// and is the only workgroup that reads those rows.
+//
+// One wave per (kv head, split, batch).  The R <= 16 query rows of a kv head
 // are the 16 columns of v_mfma_f32_16x16x32 (unused columns are zero):
 //  * S^T = K Q^T with K read straight from HBM into the A operand (16 keys x
 //    32 dims per MFMA, 16 contiguous bytes per lane);
-//  * the V rows of a 32-key step go global -> registers -> LDS (row-major,
-//    swizzled) and come back as the transposed A operand of O^T += V^T P^T
-//    through ds_read_b64_tr_b16;
-//  * the next step's K and V loads are issued before the current step's math.
+//  * the V rows of a 32-key step go global -> LDS (row-major, swizzled) by
+//    DMA and come back as the transposed A operand of O^T += V^T P^T through
+//    ds_read_b64_tr_b16;
+//  * two steps' loads are in flight while a step computes.
 // The grid is sized from the cache capacity, so the host never reads the
-// device-side cache lengths; splits past a batch's length exit at once.
+// device-side cache lengths; workgroups past the total work exit at once.
 #include "device_common.hpp"
 #include "attn_args.hpp"
 #include "launchers.hpp"
@@ -28,9 +35,119 @@ namespace attn {
 // vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14)
 #define VMCNT_WAIT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
 
-template <class T, int DQK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(64) void decode_attn_kernel(AttnArgs a) {
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+struct SeqInfo {
+  int L, off, kend;   // key length, position of query token 0, causal end of the key range
+};
+__device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b, bool causal) {
+  SeqInfo s;
+  if (a.kvcache) {
+    const int cb = a.seqlens ? a.seqlens[b] : a.seqlen_scalar;
+    s.L = cb + a.Snew;
+    s.off = cb;
+  } else {
+    s.L = a.Sk;
+    s.off = a.Sk - a.Sq;
+  }
+  s.kend = causal ? max(0, min(s.L, s.off + a.Sq)) : s.L;
+  return s;
+}
+
+// Combine the nvalid splits of query row r of (b, hkv) (one wave).  A lane
+// owns output columns lane and lane + 64.  The partial outputs of the first
+// 32 splits are requested together with the splits' maxima, so the common
+// case needs one round trip to memory; split weights are broadcast with
+// cross-lane reads.
+template <class T>
+__device__ void merge_row(const AttnArgs& a, int b, int hkv, int r, int R, int nvalid, int DV) {
+  constexpr int C = 32;
+  const int lane = threadIdx.x;
+  const int dv0 = min(lane, DV - 1), dv1 = min(lane + 64, DV - 1);   // clamped: loads never branch
+  const int tok = r / a.group;
+  const int hq = hkv * a.group + (r - tok * a.group);
+  const int64_t slot0 = ((int64_t)b * a.Hkv + hkv) * a.num_splits * R + r;
+  auto orow_of = [&](int sp) { return a.ws_o + (slot0 + (int64_t)sp * R) * DV; };
+  float v0[C], v1[C];
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const float* os = orow_of(min(j, nvalid - 1));
+    v0[j] = os[dv0];
+    v1[j] = os[dv1];
+  }
+  float M = -__builtin_inff();
+  for (int sp = lane; sp < nvalid; sp += 64) M = fmaxf(M, a.ws_ml[(slot0 + (int64_t)sp * R) * 2]);
+  M = wave_max(M);
+  const float Ms = (M == -__builtin_inff()) ? 0.f : M;
+  float lpart = 0.f, acc0 = 0.f, acc1 = 0.f;
+  for (int s0 = 0; s0 < nvalid; s0 += 64) {
+    // weight of split s0 + lane
+    const int sp = s0 + lane;
+    float w = 0.f;
+    if (sp < nvalid) {
+      const float ms = a.ws_ml[(slot0 + (int64_t)sp * R) * 2];
+      w = (ms == -__builtin_inff()) ? 0.f : fast_exp2(ms - Ms);
+      lpart += w * a.ws_ml[(slot0 + (int64_t)sp * R) * 2 + 1];
+    }
+    const int n = min(64, nvalid - s0);
+    for (int j0 = 0; j0 < n; j0 += C) {
+      if (s0 + j0 > 0) {
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+          const float* os = orow_of(s0 + min(j0 + j, n - 1));
+          v0[j] = os[dv0];
+          v1[j] = os[dv1];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        const float wj = __shfl(w, j0 + j);
+        if (j0 + j < n) {
+          acc0 += wj * v0[j];
+          acc1 += wj * v1[j];
+        }
+      }
+    }
+  }
+  const float lsum = wave_sum(lpart);
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  uint16_t* orow = a.out + (int64_t)b * a.o_sb + (int64_t)tok * a.o_ss + (int64_t)hq * a.o_sh;
+  if (lane < DV) orow[lane] = T::from_f32(acc0 * inv);
+  if (lane + 64 < DV) orow[lane + 64] = T::from_f32(acc1 * inv);
+  if (a.lse && lane == 0)
+    a.lse[((int64_t)b * a.Hq + hq) * a.Sq + tok] =
+        lsum > 0.f ? (M + __log2f(lsum)) * 0.69314718055994531f : -__builtin_inff();
+}
+
+// One wave per (batch, kv head, query row).  A (batch, kv head) whose keys
+// fit in one split (or that has no key) was finished by the attention kernel.
+template <class T>
+__global__ __launch_bounds__(64) void split_merge_kernel(AttnArgs a, int DV) {
+  const int R = a.group * a.Sq;
+  int idx = blockIdx.x;
+  const int r = idx % R;
+  idx /= R;
+  const int hkv = idx % a.Hkv;
+  const int b = idx / a.Hkv;
+  const SeqInfo si = seq_info(a, b, a.causal != 0);
+  const int nvalid = min(a.num_splits, (si.kend + a.split_len - 1) / a.split_len);
+  if (nvalid <= 1) return;
+  merge_row<T>(a, b, hkv, r, R, nvalid, DV);
+}
+
+template <class T, int DQK, int DV, bool CAUSAL, bool FUSED>
+__global__ __launch_bounds__(64, (DQK > 128 ? 1 : 2)) void decode_attn_kernel(AttnArgs a) {
   constexpr int QS = (DQK + 31) / 32;          // 32-dim k-steps of S
+  constexpr int CK = DQK / 8;                  // chunks per K row
   constexpr int CV = DV / 8;                   // chunks per V row
   constexpr int VPL = (32 * CV) / 64;          // V DMA instructions per 32-key step
   constexpr int DVB = DV / 16;                 // 16-wide output blocks
@@ -39,23 +156,24 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[3 * 32 * DV];
 
   const int lane = threadIdx.x;
-  // kv heads vary fastest across workgroups, so the heads of one split (whose
-  // rows share cache lines and DRAM pages) are fetched at about the same time
-  const int hkv = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
-  int L, off;
-  if (a.kvcache) {
-    const int cb = a.seqlens ? a.seqlens[b] : a.seqlen_scalar;
-    L = cb + a.Snew;
-    off = cb;
-  } else {
-    L = a.Sk;
-    off = a.Sk - a.Sq;
+  // Workgroup i takes the i-th (batch, split, kv head) that has keys, in that
+  // order, so the busy workgroups are the first ones dispatched and spread
+  // evenly over the CUs whatever the cache lengths; kv heads vary fastest, so
+  // the heads of one split (whose rows share cache lines and DRAM pages) are
+  // fetched at about the same time.  Batches without keys get one workgroup
+  // per kv head (split 0) that writes zeros.
+  int item = blockIdx.x;
+  int b = 0, nsp_b = 0;
+  for (; b < a.B; ++b) {
+    const SeqInfo sb = seq_info(a, b, CAUSAL);
+    nsp_b = max(1, min(a.num_splits, (sb.kend + a.split_len - 1) / a.split_len));
+    if (item < nsp_b * a.Hkv) break;
+    item -= nsp_b * a.Hkv;
   }
-  const int kend_all = CAUSAL ? max(0, min(L, off + a.Sq)) : L;
-  const int k_begin = split * a.split_len;
-  if (k_begin >= kend_all) return;
-  const int k_end = min(kend_all, k_begin + a.split_len);
-
+  if (b >= a.B) return;   // surplus workgroup
+  const int split = item / a.Hkv, hkv = item - split * a.Hkv;
+  const SeqInfo si = seq_info(a, b, CAUSAL);
+  const int L = si.L, off = si.off, kend_all = si.kend;
   const int R = a.group * a.Sq;
   const int r = lane & 15, kg = lane >> 4;
   const int tok = r / a.group;
@@ -63,17 +181,39 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(AttnArgs a) {
   const bool row_ok = r < R;
   const int qpos = off + tok;
 
-  u32x4 qf[QS];
+  const int k_begin = split * a.split_len;
+  if (k_begin >= kend_all) {
+    if (kend_all == 0 && split == 0 && row_ok) {
+      // no keys at all: the output rows are zero and the lse is -inf
+      uint16_t* orow = a.out + (int64_t)b * a.o_sb + (int64_t)tok * a.o_ss + (int64_t)hq * a.o_sh;
 #pragma unroll
-  for (int st = 0; st < QS; ++st) {
-    const int d = min(32 * st + 8 * kg, DQK - 8);
+      for (int i = 0; i < DVB; ++i) *reinterpret_cast<u32x2*>(orow + i * 16 + 4 * kg) = (u32x2){0u, 0u};
+      if (a.lse && kg == 0) a.lse[((int64_t)b * a.Hq + hq) * a.Sq + tok] = -__builtin_inff();
+    }
+    return;
+  }
+  const int k_end = min(kend_all, k_begin + a.split_len);
+  const int nvalid = min(a.num_splits, (kend_all + a.split_len - 1) / a.split_len);
+
+  u32x4 qf[QS];
+  {
     const int tq = min(tok, a.Sq - 1);
-    qf[st] = ldg16(a.q + (int64_t)b * a.q_sb + (int64_t)tq * a.q_ss + (int64_t)min(hq, a.Hq - 1) * a.q_sh + d);
-    if (!row_ok || 32 * st + 8 * kg >= DQK) qf[st] = (u32x4){0, 0, 0, 0};
+    const uint16_t* qrow = a.q + (int64_t)b * a.q_sb + (int64_t)tq * a.q_ss + (int64_t)min(hq, a.Hq - 1) * a.q_sh;
+#pragma unroll
+    for (int st = 0; st < QS; ++st) {
+      const int d = min(32 * st + 8 * kg, DQK - 8);
+      if (FUSED)
+        qf[st] = rope_chunk<T>(qrow, d, a.rcos, a.rsin, (int64_t)off + tq, a.rd, a.rinter, false);
+      else
+        qf[st] = ldg16(qrow + d);
+      if (!row_ok || 32 * st + 8 * kg >= DQK) qf[st] = (u32x4){0, 0, 0, 0};
+    }
   }
 
   const uint16_t* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
   const uint16_t* vbase = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+  const uint16_t* knbase = FUSED ? a.kn + (int64_t)b * a.kn_sb + (int64_t)hkv * a.kn_sh : nullptr;
+  const uint16_t* vnbase = FUSED ? a.vn + (int64_t)b * a.vn_sb + (int64_t)hkv * a.vn_sh : nullptr;
 
   // One 32-key step: K straight into MFMA A operands (registers), V into an
   // LDS stage by DMA.  Rows past the split end are fetched from its last row
@@ -166,6 +306,27 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(AttnArgs a) {
     }
   };
 
+  // fused append: the split whose range holds positions [c_b, L) first writes
+  // the rotated keys and the values of those rows into the cache, then reads
+  // them back like any other row (no other split reads them)
+  if (FUSED) {
+    const int n0 = max(off, k_begin), n1 = min(L, k_end);
+    if (n0 < n1) {
+      uint16_t* kc = const_cast<uint16_t*>(kbase);
+      uint16_t* vc = const_cast<uint16_t*>(vbase);
+      for (int id = lane; id < (n1 - n0) * CK; id += 64) {
+        const int key = n0 + id / CK, d = (id % CK) * 8;
+        stg16(kc + (int64_t)key * a.k_ss + d,
+              rope_chunk<T>(knbase + (int64_t)(key - off) * a.kn_ss, d, a.rcos, a.rsin, key, a.rd, a.rinter, false));
+      }
+      for (int id = lane; id < (n1 - n0) * CV; id += 64) {
+        const int key = n0 + id / CV, d = (id % CV) * 8;
+        stg16(vc + (int64_t)key * a.v_ss + d, ldg16(vnbase + (int64_t)(key - off) * a.vn_ss + d));
+      }
+      __syncthreads();   // stores complete and visible to the whole (single-wave) workgroup
+    }
+  }
+
   // three-deep pipeline: K registers A/B/C and LDS stages 0/1/2; two steps'
   // loads are in flight while the current step computes
   KBuf A, B, C;
@@ -188,6 +349,21 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(AttnArgs a) {
 
   float lt = l_run + __shfl_xor(l_run, 16);
   lt = xhalf_sum(lt);
+  if (nvalid == 1) {
+    // the only split of this (batch, kv head): normalise and store
+    if (row_ok) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      uint16_t* orow = a.out + (int64_t)b * a.o_sb + (int64_t)tok * a.o_ss + (int64_t)hq * a.o_sh;
+#pragma unroll
+      for (int i = 0; i < DVB; ++i)
+        *reinterpret_cast<u32x2*>(orow + i * 16 + 4 * kg) =
+            (u32x2){T::pack2(o[i][0] * inv, o[i][1] * inv), T::pack2(o[i][2] * inv, o[i][3] * inv)};
+      if (a.lse && kg == 0)
+        a.lse[((int64_t)b * a.Hq + hq) * a.Sq + tok] =
+            lt > 0.f ? (m_run + __log2f(lt)) * 0.69314718055994531f : -__builtin_inff();
+    }
+    return;
+  }
   if (row_ok) {
     const int64_t slot = (((int64_t)b * a.Hkv + hkv) * a.num_splits + split) * R + r;
     float* wo = a.ws_o + slot * DV;
@@ -201,102 +377,23 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(AttnArgs a) {
   }
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
-  return x;
-}
-
-// One wave per (batch, kv head, query row of that kv head): the splits'
-// maxima are reduced across lanes, then every lane accumulates its output
-// columns over the splits with independent (pipelined) loads.
-template <class T>
-__global__ __launch_bounds__(64) void split_merge_kernel(AttnArgs a, int DV) {
-  __shared__ float wsh[64];
-  const int R = a.group * a.Sq;
-  int idx = blockIdx.x;
-  const int r = idx % R;
-  idx /= R;
-  const int hkv = idx % a.Hkv;
-  const int b = idx / a.Hkv;
-  const int lane = threadIdx.x;
-  int L, off;
-  if (a.kvcache) {
-    const int cb = a.seqlens ? a.seqlens[b] : a.seqlen_scalar;
-    L = cb + a.Snew;
-    off = cb;
-  } else {
-    L = a.Sk;
-    off = a.Sk - a.Sq;
-  }
-  const int kend_all = a.causal ? max(0, min(L, off + a.Sq)) : L;
-  const int nvalid = min(a.num_splits, (kend_all + a.split_len - 1) / a.split_len);
-  const int tok = r / a.group;
-  const int hq = hkv * a.group + (r - tok * a.group);
-  const int64_t slot0 = ((int64_t)b * a.Hkv + hkv) * a.num_splits * R + r;
-
-  float M = -__builtin_inff();
-  for (int s = lane; s < nvalid; s += 64) M = fmaxf(M, a.ws_ml[(slot0 + (int64_t)s * R) * 2]);
-  M = wave_max(M);
-  const float Ms = (M == -__builtin_inff()) ? 0.f : M;
-  float lpart = 0.f;
-  float acc0 = 0.f, acc1 = 0.f;
-  const int dv0 = min(lane, DV - 1), dv1 = min(lane + 64, DV - 1);   // clamped: loads never branch
-  for (int s0 = 0; s0 < nvalid; s0 += 64) {
-    const int s = s0 + lane;
-    float w = 0.f;
-    if (s < nvalid) {
-      const float ms = a.ws_ml[(slot0 + (int64_t)s * R) * 2];
-      w = (ms == -__builtin_inff()) ? 0.f : fast_exp2(ms - Ms);
-      lpart += w * a.ws_ml[(slot0 + (int64_t)s * R) * 2 + 1];
-    }
-    __syncthreads();
-    wsh[lane] = w;
-    __syncthreads();
-    const int n = min(64, nvalid - s0);
-    for (int j0 = 0; j0 < n; j0 += 16) {
-      float v0[16], v1[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {   // 32 independent loads in flight per lane
-        const int sj = s0 + min(j0 + j, n - 1);
-        const float* os = a.ws_o + (slot0 + (int64_t)sj * R) * DV;
-        v0[j] = os[dv0];
-        v1[j] = os[dv1];
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float wj = (j0 + j < n) ? wsh[j0 + j] : 0.f;
-        acc0 += wj * v0[j];
-        acc1 += wj * v1[j];
-      }
-    }
-  }
-  const float lsum = wave_sum(lpart);
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  uint16_t* orow = a.out + (int64_t)b * a.o_sb + (int64_t)tok * a.o_ss + (int64_t)hq * a.o_sh;
-  if (lane < DV) orow[lane] = T::from_f32(acc0 * inv);
-  if (lane + 64 < DV) orow[lane + 64] = T::from_f32(acc1 * inv);
-  if (a.lse && lane == 0)
-    a.lse[((int64_t)b * a.Hq + hq) * a.Sq + tok] =
-        lsum > 0.f ? (M + __log2f(lsum)) * 0.69314718055994531f : -__builtin_inff();
-}
-
 // ---------------------------------------------------------------- launchers
 template <class T, int DQK, int DV>
-static hipError_t launch_decode(const AttnArgs& a0, bool causal, hipStream_t st) {
-  AttnArgs a = a0;
-  dim3 grid((unsigned)a.Hkv, (unsigned)a.num_splits, (unsigned)a.B);
-  if (causal)
-    hipLaunchKernelGGL((decode_attn_kernel<T, DQK, DV, true>), grid, dim3(64), 0, st, a);
-  else
-    hipLaunchKernelGGL((decode_attn_kernel<T, DQK, DV, false>), grid, dim3(64), 0, st, a);
+static hipError_t launch_decode(const AttnArgs& a, bool causal, hipStream_t st) {
+  const dim3 grid((unsigned)(a.Hkv * a.num_splits * a.B));
+  if (a.fused) {
+    if (causal)
+      hipLaunchKernelGGL((decode_attn_kernel<T, DQK, DV, true, true>), grid, dim3(64), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_attn_kernel<T, DQK, DV, false, true>), grid, dim3(64), 0, st, a);
+  } else {
+    if (causal)
+      hipLaunchKernelGGL((decode_attn_kernel<T, DQK, DV, true, false>), grid, dim3(64), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_attn_kernel<T, DQK, DV, false, false>), grid, dim3(64), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.num_splits <= 1) return e;
   const int64_t rows = (int64_t)a.B * a.Hkv * a.group * a.Sq;
   hipLaunchKernelGGL((split_merge_kernel<T>), dim3((unsigned)rows), dim3(64), 0, st, a, DV);
   return hipGetLastError();

@@ -108,6 +108,69 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// One rotated 16-bit element: the first member of a pair gives x1*c - x2*s,
+// the second x1*s + x2*c.  Both products of 16-bit inputs are exact in fp32,
+// so the fp32 result is the exact value rounded once; it is then rounded to
+// the storage type.  The empty asm keeps the compiler from fusing the fp32
+// operation and the 16-bit conversion into one mixed-precision instruction
+// (which would round the exact value straight to 16 bits).
+template <class T>
+__device__ __forceinline__ uint16_t rot_one(uint16_t x1b, uint16_t x2b, uint16_t cb, uint16_t sb, bool second,
+                                            bool conj) {
+  const float x1 = T::to_f32(x1b), x2 = T::to_f32(x2b), c = T::to_f32(cb);
+  float sn = T::to_f32(sb);
+  if (conj) sn = -sn;
+  float y = second ? x1 * sn + x2 * c : x1 * c - x2 * sn;
+  asm volatile("" : "+v"(y));
+  return T::from_f32(y);
+}
+
+// Elements [d0, d0 + 8) of row x after rotary embedding at table row `pos`:
+// the first rd dims are rotated in pairs (2j, 2j+1) when interleaved, else
+// (j, j + rd/2); the rest are copied.  Needs d0 % 8 == 0, rd % 16 == 0 and
+// 16-byte aligned rows of the [*, rd/2] cos/sin tables.  Every load of the
+// row happens before the result exists, so callers may store it in place.
+template <class T>
+__device__ __forceinline__ u32x4 rope_chunk(const uint16_t* x, int d0, const uint16_t* cos_t,
+                                            const uint16_t* sin_t, int64_t pos, int rd, bool interleaved,
+                                            bool conj) {
+  const u32x4 xv = ldg16(x + d0);
+  if (d0 >= rd) return xv;
+  const int half = rd >> 1;
+  u32x4 out;
+  if (interleaved) {
+    const u32x2 cc = *reinterpret_cast<const u32x2*>(cos_t + pos * half + (d0 >> 1));
+    const u32x2 sv = *reinterpret_cast<const u32x2*>(sin_t + pos * half + (d0 >> 1));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint16_t x1 = (uint16_t)(xv[e] & 0xFFFFu), x2 = (uint16_t)(xv[e] >> 16);
+      const uint16_t cb = (uint16_t)(cc[e >> 1] >> (16 * (e & 1)));
+      const uint16_t sb = (uint16_t)(sv[e >> 1] >> (16 * (e & 1)));
+      out[e] = (uint32_t)rot_one<T>(x1, x2, cb, sb, false, conj) |
+               ((uint32_t)rot_one<T>(x1, x2, cb, sb, true, conj) << 16);
+    }
+  } else {
+    const bool second = d0 >= half;
+    const int j0 = second ? d0 - half : d0;
+    const u32x4 pv = ldg16(x + (second ? d0 - half : d0 + half));
+    const u32x4 cc = ldg16(cos_t + pos * half + j0);
+    const u32x4 sv = ldg16(sin_t + pos * half + j0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t own = (uint16_t)(xv[e >> 1] >> (16 * (e & 1)));
+      const uint16_t oth = (uint16_t)(pv[e >> 1] >> (16 * (e & 1)));
+      const uint16_t cb = (uint16_t)(cc[e >> 1] >> (16 * (e & 1)));
+      const uint16_t sb = (uint16_t)(sv[e >> 1] >> (16 * (e & 1)));
+      const uint16_t r = second ? rot_one<T>(oth, own, cb, sb, true, conj) : rot_one<T>(own, oth, cb, sb, false, conj);
+      if (e & 1)
+        out[e >> 1] |= (uint32_t)r << 16;
+      else
+        out[e >> 1] = r;
+    }
+  }
+  return out;
+}
+
 // Buffer resource over [base, base + bytes) for raw (unswizzled, stride 0)
 // loads: offsets at or past `bytes` read as zero, per dword.
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {

@@ -64,18 +64,6 @@ __device__ __forceinline__ void process_row(const RowSet& rs, int row, int lane)
   for (int d = a.rd + lane; d < a.D; d += 64) y[d] = x[d];
 }
 
-// y for one 16-bit element: first half of a pair -> x1*c - x2*s, second -> x1*s + x2*c
-template <class T>
-__device__ __forceinline__ uint16_t rot_one(uint16_t x1b, uint16_t x2b, uint16_t cb, uint16_t sb, bool second,
-                                            bool conj) {
-  const float x1 = T::to_f32(x1b), x2 = T::to_f32(x2b), c = T::to_f32(cb);
-  float sn = T::to_f32(sb);
-  if (conj) sn = -sn;
-  float y = second ? x1 * sn + x2 * c : x1 * c - x2 * sn;
-  asm volatile("" : "+v"(y));   // round the exact value to fp32 first (see process_row)
-  return T::from_f32(y);
-}
-
 template <class T>
 __global__ __launch_bounds__(256) void rope_vec_kernel(RowSet s0, RowSet s1, RowSet s2) {
   const RowSet& rs = blockIdx.y == 0 ? s0 : (blockIdx.y == 1 ? s1 : s2);
@@ -98,49 +86,8 @@ __global__ __launch_bounds__(256) void rope_vec_kernel(RowSet s0, RowSet s1, Row
   const uint16_t* x = a.x + (int64_t)b * a.x_sb + (int64_t)s * a.x_ss + (int64_t)h * a.x_sh;
   uint16_t* y = a.y + (int64_t)b * a.y_sb + (int64_t)ds * a.y_ss + (int64_t)h * a.y_sh;
   const int d0 = c * 8;
-  const u32x4 xv = ldg16(x + d0);
-  if (a.copy_only || d0 >= a.rd) {
-    stg16(y + d0, xv);
-    return;
-  }
-  const int half = a.rd >> 1;
-  const int64_t pos = off + s;
-  u32x4 out;
-  if (a.interleaved) {
-    // elements 2e, 2e+1 of the chunk form pair d0/2 + e
-    const u32x2 cc = *reinterpret_cast<const u32x2*>(a.cos + pos * half + (d0 >> 1));
-    const u32x2 sv = *reinterpret_cast<const u32x2*>(a.sin + pos * half + (d0 >> 1));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint16_t x1 = (uint16_t)(xv[e] & 0xFFFFu), x2 = (uint16_t)(xv[e] >> 16);
-      const uint32_t cw = cc[e >> 1], sw = sv[e >> 1];
-      const uint16_t cb = (uint16_t)((e & 1) ? cw >> 16 : cw & 0xFFFFu);
-      const uint16_t sb = (uint16_t)((e & 1) ? sw >> 16 : sw & 0xFFFFu);
-      const uint16_t y1 = rot_one<T>(x1, x2, cb, sb, false, a.conjugate);
-      const uint16_t y2 = rot_one<T>(x1, x2, cb, sb, true, a.conjugate);
-      out[e] = (uint32_t)y1 | ((uint32_t)y2 << 16);
-    }
-  } else {
-    const bool second = d0 >= half;
-    const int j0 = second ? d0 - half : d0;
-    const u32x4 pv = ldg16(x + (second ? d0 - half : d0 + half));
-    const u32x4 cc = ldg16(a.cos + pos * half + j0);
-    const u32x4 sv = ldg16(a.sin + pos * half + j0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint16_t own = (uint16_t)(xv[e >> 1] >> (16 * (e & 1)));
-      const uint16_t oth = (uint16_t)(pv[e >> 1] >> (16 * (e & 1)));
-      const uint16_t cb = (uint16_t)(cc[e >> 1] >> (16 * (e & 1)));
-      const uint16_t sb = (uint16_t)(sv[e >> 1] >> (16 * (e & 1)));
-      const uint16_t r = second ? rot_one<T>(oth, own, cb, sb, true, a.conjugate)
-                                : rot_one<T>(own, oth, cb, sb, false, a.conjugate);
-      if (e & 1)
-        out[e >> 1] |= (uint32_t)r << 16;
-      else
-        out[e >> 1] = r;
-    }
-  }
-  stg16(y + d0, out);
+  const int rd = a.copy_only ? 0 : a.rd;
+  stg16(y + d0, rope_chunk<T>(x, d0, a.cos, a.sin, (int64_t)off + s, rd, a.interleaved, a.conjugate));
 }
 
 template <class T>

@@ -141,6 +141,11 @@ int attn_fwd(const attn_fwd_params* p, void* stream);
  * bytes, 256-byte aligned (NULL allowed when that size is 0); its content on
  * entry is irrelevant.  num_splits: 0 picks the split count of the
  * single-token decode path automatically; a positive value forces it.
+ *
+ * On the single-token decode path (at most 16 query rows per kv head) the
+ * rotary embedding (when rotary_dim is a multiple of 16 and the tables are
+ * 16-byte aligned) and the append run inside the attention kernel; otherwise
+ * a separate append/rotation pass runs first.
  */
 typedef struct attn_kvcache_params {
   attn_dtype dtype;

@@ -156,20 +156,29 @@ def test_validate_kvcache_rotary_args():
     assert _code_kv(p) == -2
 
 
+def _al(x):
+    return (x + 255) // 256 * 256
+
+
 def test_kvcache_workspace_plan():
-    # decode path: partials for every (batch, kv head, split, row) plus rotated q
+    # decode path: partials for every (batch, kv head, split, row); the
+    # rotation happens inside the decode kernel (rd % 16 == 0)
     p, keep = _kv(B=8, Hq=32, Hkv=8, D=128, cap=8192, rotary=128)
     need = E.kvcache_workspace_size(p)
     split = 256
     nsp = 8192 // split
     R = 4
-    q_rot = 8 * 1 * 32 * 128 * 2
-    expect = q_rot + 8 * 8 * nsp * R * 128 * 4
-    expect = ((expect + 255) // 256) * 256 + ((8 * 8 * nsp * R * 2 * 4 + 255) // 256) * 256
-    assert need == expect
+    cnt = 0
+    assert need == cnt + _al(8 * 8 * nsp * R * 128 * 4) + _al(8 * 8 * nsp * R * 2 * 4)
     # forcing one split
     p.num_splits = 1
-    assert E.kvcache_workspace_size(p) == q_rot + 8 * 8 * 1 * R * 128 * 4 + 8 * 8 * R * 2 * 4
+    assert E.kvcache_workspace_size(p) == cnt + _al(8 * 8 * 1 * R * 128 * 4) + _al(8 * 8 * R * 2 * 4)
+    # a rotary width that is not a multiple of 16 takes the separate rotation
+    # pass, whose rotated q copy comes first
+    p, keep = _kv(B=8, Hq=32, Hkv=8, D=128, cap=8192, rotary=40)
+    q_rot = 8 * 1 * 32 * 128 * 2
+    assert E.kvcache_workspace_size(p) == cnt + _al(q_rot) + _al(8 * 8 * nsp * R * 128 * 4) + \
+        _al(8 * 8 * nsp * R * 2 * 4)
     # chunked prefill (many query rows): only the rotated q copy
     p, keep = _kv(B=4, Sq=512, Hq=16, Hkv=16, D=128, cap=4096, snew=512, rotary=64)
     assert E.kvcache_workspace_size(p) == 4 * 512 * 16 * 128 * 2
