@@ -86,17 +86,28 @@ def summarize(d):
                 print("    %-32s %16.6g   (dispatches: %d)" % (cn, sum(v) / len(v), len(v)))
 
 
-def traffic_entry(kernel_key):
-    """Measured HBM bytes per launch for a kernel, if its source is unchanged since measured."""
+def sources_sha256(paths):
+    """One digest over the given source files (the kernel file and the headers it includes)."""
     import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(p.encode())
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()
+
+
+def traffic_entry(kernel_key):
+    """Measured HBM bytes per launch for a kernel, if its sources are unchanged since measured."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(kernel_key)
     if not rec:
         return None
-    src = os.path.join(ROOT, rec["source"])
-    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+    srcs = rec.get("sources", [])
+    if not srcs or not all(os.path.exists(os.path.join(ROOT, p)) for p in srcs):
+        return None
+    if sources_sha256(srcs) != rec["sources_sha256"]:
         return None
     return rec["hbm_bytes_per_launch"]
 
