@@ -16,7 +16,12 @@ Readings of points the pages leave open (listed again in the design doc):
 * grouped-query heads: q head ``h`` reads kv head ``h // (Hq // Hkv)``
   (Workflow 2 Step 3, fewer K/V heads than q heads);
 * a row with no allowed key has output 0 and lse = -inf;
-* ``lse`` is the natural-log sum of exp(scale * score) over allowed keys.
+* ``lse`` is the natural-log sum of exp(scale * score) over allowed keys;
+* local (sliding-window) attention, ``window=(left, right)`` (Workflow 2,
+  Step 3: a window of tokens before and after each query, ``(-1, -1)``
+  meaning none): the query at position p keeps key j iff
+  ``p - left <= j <= p + right``, a side given as -1 being unbounded; with
+  ``causal`` the causal test applies as well.
 """
 from __future__ import annotations
 
@@ -26,14 +31,15 @@ import numpy as np
 
 
 def attention_ref(q, k, v, *, causal: bool = False, softmax_scale=None,
-                  key_lens=None, q_pos=None):
+                  key_lens=None, q_pos=None, window=(-1, -1)):
     """Exact attention, fp64.
 
     q: [B, Sq, Hq, Dqk], k: [B, Sk, Hkv, Dqk], v: [B, Sk, Hkv, Dv] (fp64 arrays).
     key_lens: optional [B] ints; keys j >= key_lens[b] are excluded (the rows
       are sliced away, so their content -- NaN included -- never matters).
-    q_pos: optional [B, Sq] absolute query positions for the causal test
-      ``j <= q_pos[b, i]``; default ``i + Sk - Sq``.
+    q_pos: optional [B, Sq] absolute query positions for the causal and
+      window tests; default ``i + Sk - Sq``.
+    window: (left, right) local-attention window, -1 = unbounded side.
     Returns (out [B, Sq, Hq, Dv] fp64, lse [B, Hq, Sq] fp64).
     """
     q = np.asarray(q, np.float64)
@@ -54,9 +60,15 @@ def attention_ref(q, k, v, *, causal: bool = False, softmax_scale=None,
             pos = np.arange(Sq) + (L - Sq)
         else:
             pos = np.asarray(q_pos[b], np.int64)
+        keys = np.arange(L)[None, :]
         allowed = np.ones((Sq, L), bool)
         if causal:
-            allowed = np.arange(L)[None, :] <= pos[:, None]
+            allowed &= keys <= pos[:, None]
+        left, right = int(window[0]), int(window[1])
+        if left >= 0:
+            allowed &= keys >= pos[:, None] - left
+        if right >= 0:
+            allowed &= keys <= pos[:, None] + right
         for h in range(Hq):
             hk = h // group
             Kb = k[b, :L, hk, :]

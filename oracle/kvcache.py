@@ -11,7 +11,9 @@ What ``flash_attn_with_kvcache`` computes, as the pages describe it
 3. the query tokens, at positions c_b + i, are rotated with the same tables
    and rounded to the dtype; they are not written anywhere;
 4. attention of the rotated queries over cache rows [0, c_b + Snew), causal
-   on absolute position (key j allowed iff j <= c_b + i) when ``causal``.
+   on absolute position (key j allowed iff j <= c_b + i) when ``causal``,
+   and restricted to the local window around the query's absolute position
+   when ``window`` is given.
 
 Step 4 is ``attention_ref``; step 2/3's rotation is ``rope_ref`` with its
 rounding contract.
@@ -26,7 +28,7 @@ from .rope import rope_ref
 
 def kvcache_ref(q, k_cache, v_cache, k_new, v_new, cache_seqlens, *, dtype: str,
                 rotary_cos=None, rotary_sin=None, rotary_interleaved=False,
-                causal=False, softmax_scale=None):
+                causal=False, softmax_scale=None, window=(-1, -1)):
     """All array arguments are fp64 values of ``dtype`` tensors.
 
     q [B,Sq,Hq,Dqk]; k_cache [B,cap,Hkv,Dqk]; v_cache [B,cap,Hkv,Dv];
@@ -66,5 +68,5 @@ def kvcache_ref(q, k_cache, v_cache, k_new, v_new, cache_seqlens, *, dtype: str,
             vc[b, lens[b]:lens[b] + snew] = vn[b]
     key_lens = [lens[b] + snew for b in range(B)]
     out, lse = attention_ref(qr, kc, vc, causal=causal, softmax_scale=softmax_scale,
-                             key_lens=key_lens, q_pos=qpos)
+                             key_lens=key_lens, q_pos=qpos, window=window)
     return out, lse, kc, vc

@@ -140,7 +140,7 @@ def test_default_scale_uses_qk_head_dim():
     assert np.array_equal(a, b)
 
 
-def _brute_attention(q, k, v, causal, scale, key_lens=None, q_pos=None):
+def _brute_attention(q, k, v, causal, scale, key_lens=None, q_pos=None, window=(-1, -1)):
     B, Sq, Hq, Dqk = q.shape
     Sk, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
     out = np.zeros((B, Sq, Hq, Dv))
@@ -150,7 +150,11 @@ def _brute_attention(q, k, v, causal, scale, key_lens=None, q_pos=None):
             hk = h * Hkv // Hq
             for i in range(Sq):
                 pos = (i + L - Sq) if q_pos is None else q_pos[b][i]
-                keys = [j for j in range(L) if (not causal or j <= pos)]
+                # a key is kept when it is no more than `left` positions before
+                # the query and no more than `right` after it (-1: no limit)
+                keys = [j for j in range(L) if (not causal or j <= pos)
+                        and (window[0] < 0 or pos - j <= window[0])
+                        and (window[1] < 0 or j - pos <= window[1])]
                 sc = []
                 for j in keys:
                     s = 0.0
@@ -175,6 +179,57 @@ def test_brute_force_tiny(B, Sq, Sk, Hq, Hkv, Dqk, Dv, causal):
     out, _ = attention_ref(q, k, v, causal=causal, softmax_scale=0.8)
     ref = _brute_attention(q, k, v, causal, 0.8)
     assert np.allclose(out, ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- local window
+# Workflow 2, Step 3 of the skill page "Flash Attention - Fast Memory-Efficient
+# Attention": window_size=(left, right) keeps the tokens before and after each
+# query; (-1, -1) is no window.
+
+@pytest.mark.parametrize("window", [(0, 0), (1, 0), (2, 1), (0, 3), (-1, 1), (2, -1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_brute_force_tiny(window, causal):
+    q, k, v = _rand_qkv(2, 5, 6, 2, 1, 3, 2, seed=7 + window[0] * 3 + window[1])
+    out, _ = attention_ref(q, k, v, causal=causal, softmax_scale=0.7, window=window)
+    ref = _brute_attention(q, k, v, causal, 0.7, window=window)
+    assert np.allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_window_zero_keeps_only_own_position():
+    # window (0, 0): the only key of the query at position p is key p, so the
+    # output is that value row exactly (rows whose position has no key are 0)
+    q, k, v = _rand_qkv(2, 4, 6, 2, 2, 3, 5, seed=3)
+    out, lse = attention_ref(q, k, v, softmax_scale=0.9, window=(0, 0))
+    for b in range(2):
+        for i in range(4):
+            p = i + 6 - 4
+            assert np.array_equal(out[b, i], v[b, p])
+    # Sq > Sk: the first rows sit at negative positions and see no key
+    q, k, v = _rand_qkv(1, 5, 3, 1, 1, 2, 2, seed=4)
+    out, lse = attention_ref(q, k, v, window=(0, 0))
+    assert np.all(out[0, :2] == 0) and np.all(np.isneginf(lse[0, 0, :2]))
+    assert np.array_equal(out[0, 2:, 0], v[0, :, 0])
+
+
+def test_window_right_zero_is_causal_and_wide_window_is_full():
+    q, k, v = _rand_qkv(2, 6, 9, 4, 2, 4, 3, seed=11)
+    causal, _ = attention_ref(q, k, v, causal=True)
+    right0, _ = attention_ref(q, k, v, window=(-1, 0))
+    assert np.array_equal(causal, right0)
+    full, _ = attention_ref(q, k, v)
+    wide, _ = attention_ref(q, k, v, window=(9, 9))
+    assert np.array_equal(full, wide)
+
+
+def test_window_uniform_weights_average_the_window():
+    # scale 0 gives every allowed key the same weight: the output is the mean
+    # of the value rows inside the window (closed form)
+    q, k, v = _rand_qkv(1, 7, 7, 1, 1, 2, 3, seed=5)
+    left, right = 2, 1
+    out, _ = attention_ref(q, k, v, softmax_scale=0.0, window=(left, right))
+    for i in range(7):
+        lo, hi = max(0, i - left), min(7, i + right + 1)
+        assert np.allclose(out[0, i, 0], v[0, lo:hi, 0].mean(axis=0), rtol=0, atol=1e-14)
 
 
 # ---------------------------------------------------------------- rope
