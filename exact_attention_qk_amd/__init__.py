@@ -52,7 +52,8 @@ class FwdParams(ctypes.Structure):
                 ("Dqk", ctypes.c_int), ("Dv", ctypes.c_int),
                 ("q", Tensor4), ("k", Tensor4), ("v", Tensor4), ("out", Tensor4),
                 ("lse", ctypes.c_void_p), ("causal", ctypes.c_int),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float),
+                ("window_left", ctypes.c_int), ("window_right", ctypes.c_int)]
 
 
 class KVCacheParams(ctypes.Structure):
@@ -67,7 +68,8 @@ class KVCacheParams(ctypes.Structure):
                 ("rotary_interleaved", ctypes.c_int), ("causal", ctypes.c_int),
                 ("softmax_scale", ctypes.c_float), ("lse", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("num_splits", ctypes.c_int)]
+                ("num_splits", ctypes.c_int),
+                ("window_left", ctypes.c_int), ("window_right", ctypes.c_int)]
 
 
 class RopeParams(ctypes.Structure):
@@ -129,22 +131,26 @@ def _stream(t):
 
 # ---------------------------------------------------------------- attn_fwd
 
-def fwd_params(q, k, v, out, causal=False, softmax_scale=None, lse=None):
+def fwd_params(q, k, v, out, causal=False, softmax_scale=None, lse=None, window_size=(-1, -1)):
     B, Sq, Hq, Dqk = q.shape
     Sk, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
     return FwdParams(_dtype(q), B, Sq, Sk, Hq, Hkv, Dqk, Dv, _t4(q), _t4(k), _t4(v), _t4(out),
                      lse.data_ptr() if lse is not None else None, int(bool(causal)),
-                     _scale(softmax_scale))
+                     _scale(softmax_scale), int(window_size[0]), int(window_size[1]))
 
 
-def attn_fwd(q, k, v, causal=False, softmax_scale=None, out=None, return_lse=False):
-    """Exact attention.  q [B,Sq,Hq,Dqk], k [B,Sk,Hkv,Dqk], v [B,Sk,Hkv,Dv] -> out [B,Sq,Hq,Dv]."""
+def attn_fwd(q, k, v, causal=False, softmax_scale=None, out=None, return_lse=False,
+             window_size=(-1, -1)):
+    """Exact attention.  q [B,Sq,Hq,Dqk], k [B,Sk,Hkv,Dqk], v [B,Sk,Hkv,Dv] -> out [B,Sq,Hq,Dv].
+
+    ``window_size=(left, right)``: local attention, -1 for an unbounded side.
+    """
     B, Sq, Hq, _ = q.shape
     Dv = v.shape[3]
     if out is None:
         out = torch.empty((B, Sq, Hq, Dv), dtype=q.dtype, device=q.device)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
-    p = fwd_params(q, k, v, out, causal, softmax_scale, lse)
+    p = fwd_params(q, k, v, out, causal, softmax_scale, lse, window_size)
     _check(_lib.attn_fwd(ctypes.byref(p), _stream(q)))
     return (out, lse) if return_lse else out
 
@@ -153,7 +159,7 @@ def attn_fwd(q, k, v, causal=False, softmax_scale=None, out=None, return_lse=Fal
 
 def kvcache_params(q, k_cache, v_cache, k=None, v=None, rotary_cos=None, rotary_sin=None,
                    cache_seqlens=0, causal=False, softmax_scale=None, rotary_interleaved=False,
-                   out=None, lse=None, workspace=None, num_splits=0):
+                   out=None, lse=None, workspace=None, num_splits=0, window_size=(-1, -1)):
     B, Sq, Hq, Dqk = q.shape
     cap, Hkv, Dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
     snew = 0 if k is None else k.shape[1]
@@ -174,7 +180,8 @@ def kvcache_params(q, k_cache, v_cache, k=None, v=None, rotary_cos=None, rotary_
         rd, seq_ro, int(bool(rotary_interleaved)), int(bool(causal)), _scale(softmax_scale),
         lse.data_ptr() if lse is not None else None,
         workspace.data_ptr() if workspace is not None and workspace.numel() else None,
-        workspace.numel() if workspace is not None else 0, int(num_splits))
+        workspace.numel() if workspace is not None else 0, int(num_splits),
+        int(window_size[0]), int(window_size[1]))
 
 
 def kvcache_workspace_size(params: KVCacheParams) -> int:
@@ -183,10 +190,11 @@ def kvcache_workspace_size(params: KVCacheParams) -> int:
 
 def attn_fwd_kvcache(q, k_cache, v_cache, k=None, v=None, rotary_cos=None, rotary_sin=None,
                      cache_seqlens=0, causal=False, softmax_scale=None, rotary_interleaved=None,
-                     num_splits=0, out=None, return_lse=False, workspace=None):
+                     num_splits=0, out=None, return_lse=False, workspace=None, window_size=(-1, -1)):
     """flash_attn_with_kvcache: append k/v at cache_seqlens (in place), then attend.
 
     ``rotary_interleaved`` must be given whenever rotary tables are passed.
+    ``window_size=(left, right)``: local attention around each query's absolute position.
     """
     if rotary_cos is not None and rotary_interleaved is None:
         raise ValueError("rotary_interleaved must be given explicitly with rotary tables")
@@ -196,7 +204,7 @@ def attn_fwd_kvcache(q, k_cache, v_cache, k=None, v=None, rotary_cos=None, rotar
         out = torch.empty((B, Sq, Hq, Dv), dtype=q.dtype, device=q.device)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
     p = kvcache_params(q, k_cache, v_cache, k, v, rotary_cos, rotary_sin, cache_seqlens, causal,
-                       softmax_scale, bool(rotary_interleaved), out, lse, None, num_splits)
+                       softmax_scale, bool(rotary_interleaved), out, lse, None, num_splits, window_size)
     need = kvcache_workspace_size(p)
     if workspace is None or workspace.numel() < need + 256:
         workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
@@ -249,16 +257,16 @@ class PreparedCall:
             _check(code)
 
 
-def prepare_fwd(q, k, v, out, causal=False, softmax_scale=None, lse=None):
-    p = fwd_params(q, k, v, out, causal, softmax_scale, lse)
+def prepare_fwd(q, k, v, out, causal=False, softmax_scale=None, lse=None, window_size=(-1, -1)):
+    p = fwd_params(q, k, v, out, causal, softmax_scale, lse, window_size)
     return PreparedCall(_lib.attn_fwd, p, _stream(q), (q, k, v, out, lse))
 
 
 def prepare_kvcache(q, k_cache, v_cache, k, v, out, *, rotary_cos=None, rotary_sin=None,
                     cache_seqlens=0, causal=False, softmax_scale=None, rotary_interleaved=False,
-                    num_splits=0, lse=None):
+                    num_splits=0, lse=None, window_size=(-1, -1)):
     p = kvcache_params(q, k_cache, v_cache, k, v, rotary_cos, rotary_sin, cache_seqlens, causal,
-                       softmax_scale, rotary_interleaved, out, lse, None, num_splits)
+                       softmax_scale, rotary_interleaved, out, lse, None, num_splits, window_size)
     need = kvcache_workspace_size(p)
     ws = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
     off = (-ws.data_ptr()) % 256

@@ -77,6 +77,12 @@ void set_k(attn::AttnArgs& a, const attn_tensor4& t) {
 void set_v(attn::AttnArgs& a, const attn_tensor4& t) {
   a.v = static_cast<const uint16_t*>(t.data); a.v_sb = t.stride_b; a.v_ss = t.stride_s; a.v_sh = t.stride_h;
 }
+// -1 (unbounded) becomes a distance no position can exceed
+void set_window(attn::AttnArgs& a, int left, int right) {
+  a.wl = (left < 0 || left > attn::kNoWindow) ? attn::kNoWindow : left;
+  a.wr = (right < 0 || right > attn::kNoWindow) ? attn::kNoWindow : right;
+}
+
 void set_o(attn::AttnArgs& a, const attn_tensor4& t) {
   a.out = static_cast<uint16_t*>(t.data); a.o_sb = t.stride_b; a.o_ss = t.stride_s; a.o_sh = t.stride_h;
 }
@@ -139,11 +145,15 @@ int validate_fwd(const attn_fwd_params* p) {
   if ((e = check_dtype(p->dtype))) return e;
   if (p->B < 0 || p->Sq < 0 || p->Sk < 0 || p->Hq < 1 || p->Hkv < 1)
     return fail(ATTN_E_SHAPE, "sizes must satisfy B, Sq, Sk >= 0 and Hq, Hkv >= 1");
+  if (p->Sq >= attn::kNoWindow || p->Sk >= attn::kNoWindow)
+    return fail(ATTN_E_SHAPE, "sequence lengths must be below 2^29");
   if (p->Hq % p->Hkv)
     return fail(ATTN_E_SHAPE, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
   if (!dims_supported(p->Dqk, p->Dv))
     return fail(ATTN_E_UNSUPPORTED, "(Dqk, Dv) = (%d, %d) is not one of (16,16), (64,64), (128,128), (192,128)",
                 p->Dqk, p->Dv);
+  if (p->window_left < -1 || p->window_right < -1)
+    return fail(ATTN_E_SHAPE, "window (%d, %d): each side must be >= -1", p->window_left, p->window_right);
   if (p->B == 0 || p->Sq == 0) return ok();
   if ((e = check_tensor(p->q, "q"))) return e;
   if (p->Sk > 0) {
@@ -160,6 +170,8 @@ int validate_kvcache(const attn_kvcache_params* p) {
   if ((e = check_dtype(p->dtype))) return e;
   if (p->B < 0 || p->Sq < 0 || p->Hq < 1 || p->Hkv < 1 || p->capacity < 1 || p->Snew < 0)
     return fail(ATTN_E_SHAPE, "sizes must satisfy B, Sq, Snew >= 0 and Hq, Hkv, capacity >= 1");
+  if (p->Sq >= attn::kNoWindow || p->capacity >= attn::kNoWindow)
+    return fail(ATTN_E_SHAPE, "sequence lengths must be below 2^29");
   if (p->Hq % p->Hkv)
     return fail(ATTN_E_SHAPE, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
   if (!dims_supported(p->Dqk, p->Dv))
@@ -167,6 +179,8 @@ int validate_kvcache(const attn_kvcache_params* p) {
                 p->Dqk, p->Dv);
   if (p->Snew != 0 && p->Snew != p->Sq)
     return fail(ATTN_E_SHAPE, "Snew (%d) must be 0 or equal to Sq (%d)", p->Snew, p->Sq);
+  if (p->window_left < -1 || p->window_right < -1)
+    return fail(ATTN_E_SHAPE, "window (%d, %d): each side must be >= -1", p->window_left, p->window_right);
   if (p->Snew > p->capacity)
     return fail(ATTN_E_OVERFLOW, "Snew (%d) exceeds the cache capacity (%d)", p->Snew, p->capacity);
   if (!p->cache_seqlens) {
@@ -246,7 +260,7 @@ int hip_fail(hipError_t e, const char* what) {
 
 extern "C" {
 
-int attn_abi_version(void) { return 1; }
+int attn_abi_version(void) { return 2; }
 
 const char* attn_last_error(void) { return g_err.c_str(); }
 
@@ -264,6 +278,7 @@ int attn_fwd(const attn_fwd_params* p, void* stream) {
   a.B = p->B; a.Sq = p->Sq; a.Sk = p->Sk; a.Hq = p->Hq; a.Hkv = p->Hkv; a.group = p->Hq / p->Hkv;
   a.kvcache = 0;
   a.causal = p->causal ? 1 : 0;
+  set_window(a, p->window_left, p->window_right);
   a.c = resolve_c(p->softmax_scale, p->Dqk);
   hipError_t he = attn::run_tile_attn(a, p->dtype == ATTN_DTYPE_BF16, p->Dqk, p->Dv, p->causal != 0,
                                       static_cast<hipStream_t>(stream));
@@ -358,6 +373,7 @@ int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream) {
   a.Snew = p->Snew;
   a.kvcache = 1;
   a.causal = p->causal ? 1 : 0;
+  set_window(a, p->window_left, p->window_right);
   a.c = resolve_c(p->softmax_scale, p->Dqk);
   hipError_t he;
   if (plan.decode) {

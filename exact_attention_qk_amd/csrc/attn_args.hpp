@@ -4,6 +4,8 @@
 
 namespace attn {
 
+constexpr int kNoWindow = 1 << 29;   // window side without a limit (positions stay far below)
+
 struct AttnArgs {
   const uint16_t* q;  int64_t q_sb, q_ss, q_sh;
   const uint16_t* k;  int64_t k_sb, k_ss, k_sh;
@@ -16,6 +18,8 @@ struct AttnArgs {
   int kvcache;                // 1: key length c_b + Snew, query i at c_b + i
                               // 0: key length Sk, query i at i + Sk - Sq
   int causal;                 // key j allowed for query i iff j <= position(i)
+  int wl, wr;                 // local window: key j allowed iff pos - wl <= j <= pos + wr
+                              // (kNoWindow when a side is unbounded)
   int num_qtiles;             // tiled kernel: ceil(Sq / rows per workgroup)
   int xcd_remap;              // tiled kernel: 1 when the grid is a multiple of 8
   float c;                    // softmax_scale * log2(e)

@@ -46,8 +46,11 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Keys of a batch that any of its query rows can see: [kbeg, kend), with
+// the query at position p seeing p - wl <= j <= p + wr (wr capped at 0 when
+// causal).  Splits tile [kbeg, kend).
 struct SeqInfo {
-  int L, off, kend;   // key length, position of query token 0, causal end of the key range
+  int L, off, kbeg, kend, wl, wr;   // key length, position of query token 0, key range, window
 };
 __device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b, bool causal) {
   SeqInfo s;
@@ -59,8 +62,14 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b, bool causa
     s.L = a.Sk;
     s.off = a.Sk - a.Sq;
   }
-  s.kend = causal ? max(0, min(s.L, s.off + a.Sq)) : s.L;
+  s.wl = a.wl;
+  s.wr = causal ? min(a.wr, 0) : a.wr;
+  s.kend = max(0, min(s.L, s.off + a.Sq + s.wr));
+  s.kbeg = min(s.kend, max(0, s.off - s.wl));
   return s;
+}
+__device__ __forceinline__ int split_count(const AttnArgs& a, const SeqInfo& s) {
+  return min(a.num_splits, (s.kend - s.kbeg + a.split_len - 1) / a.split_len);
 }
 
 // Combine the nvalid splits of query row r of (b, hkv) (one wave).  A lane
@@ -139,7 +148,7 @@ __global__ __launch_bounds__(64) void split_merge_kernel(AttnArgs a, int DV) {
   const int hkv = idx % a.Hkv;
   const int b = idx / a.Hkv;
   const SeqInfo si = seq_info(a, b, a.causal != 0);
-  const int nvalid = min(a.num_splits, (si.kend + a.split_len - 1) / a.split_len);
+  const int nvalid = split_count(a, si);
   if (nvalid <= 1) return;
   merge_row<T>(a, b, hkv, r, R, nvalid, DV);
 }
@@ -166,14 +175,14 @@ __global__ __launch_bounds__(64, (DQK > 128 ? 1 : 2)) void decode_attn_kernel(At
   int b = 0, nsp_b = 0;
   for (; b < a.B; ++b) {
     const SeqInfo sb = seq_info(a, b, CAUSAL);
-    nsp_b = max(1, min(a.num_splits, (sb.kend + a.split_len - 1) / a.split_len));
+    nsp_b = max(1, split_count(a, sb));
     if (item < nsp_b * a.Hkv) break;
     item -= nsp_b * a.Hkv;
   }
   if (b >= a.B) return;   // surplus workgroup
   const int split = item / a.Hkv, hkv = item - split * a.Hkv;
   const SeqInfo si = seq_info(a, b, CAUSAL);
-  const int L = si.L, off = si.off, kend_all = si.kend;
+  const int L = si.L, off = si.off, kend_all = si.kend, wlft = si.wl, wrgt = si.wr;
   const int R = a.group * a.Sq;
   const int r = lane & 15, kg = lane >> 4;
   const int tok = r / a.group;
@@ -181,9 +190,9 @@ __global__ __launch_bounds__(64, (DQK > 128 ? 1 : 2)) void decode_attn_kernel(At
   const bool row_ok = r < R;
   const int qpos = off + tok;
 
-  const int k_begin = split * a.split_len;
+  const int k_begin = si.kbeg + split * a.split_len;
   if (k_begin >= kend_all) {
-    if (kend_all == 0 && split == 0 && row_ok) {
+    if (kend_all == si.kbeg && split == 0 && row_ok) {
       // no keys at all: the output rows are zero and the lse is -inf
       uint16_t* orow = a.out + (int64_t)b * a.o_sb + (int64_t)tok * a.o_ss + (int64_t)hq * a.o_sh;
 #pragma unroll
@@ -193,7 +202,7 @@ __global__ __launch_bounds__(64, (DQK > 128 ? 1 : 2)) void decode_attn_kernel(At
     return;
   }
   const int k_end = min(kend_all, k_begin + a.split_len);
-  const int nvalid = min(a.num_splits, (kend_all + a.split_len - 1) / a.split_len);
+  const int nvalid = split_count(a, si);
 
   u32x4 qf[QS];
   {
@@ -270,7 +279,7 @@ __global__ __launch_bounds__(64, (DQK > 128 ? 1 : 2)) void decode_attn_kernel(At
     for (int i = 0; i < 8; ++i) {
       const int key = kk + (i < 4 ? 4 * kg + i : 16 + 4 * kg + i - 4);
       const float v = (i < 4 ? sa[i] : sb[i - 4]) * c;
-      const bool ok = key < k_end && (!CAUSAL || key <= qpos);
+      const bool ok = key < k_end && key <= qpos + wrgt && key >= qpos - wlft;
       x[i] = ok ? v : -__builtin_inff();
       mx = fmaxf(mx, x[i]);
     }

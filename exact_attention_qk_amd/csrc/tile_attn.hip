@@ -31,8 +31,9 @@
 //    max exceeds it by more than 2^8, so the O rescale is rare and P stays
 //    below 256; the row sum is accumulated from the packed P with v_dot2, so
 //    numerator and denominator use the same rounded weights;
-//  * causal: waves skip 32-key blocks above their rows' diagonal and mask only
-//    blocks that cross it;
+//  * causal and local windows: a unit walks only the key tiles its rows can
+//    see, waves skip 32-key blocks outside their rows' band and mask only
+//    blocks that cross a band edge;
 //  * epilogue: O / l rounded to the output type, staged through LDS so each
 //    lane stores 16 contiguous bytes of an output row.
 #include "device_common.hpp"
@@ -73,8 +74,8 @@ __device__ __forceinline__ float dot2_sum<BF16>(uint32_t p, float acc) {
                                          (bf16x2){(__bf16)1.f, (__bf16)1.f}, acc, false);
 }
 
-template <class T, int DQK, int DV, bool CAUSAL, int RB, int NR, int NS, int BN, bool PAIR, bool FASTC,
-          int MINW>
+template <class T, int DQK, int DV, bool CAUSAL, bool WIN, int RB, int NR, int NS, int BN, bool PAIR,
+          bool FASTC, int MINW>
 __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs a) {
   constexpr int NKB = BN / 32;                           // 32-key MFMA blocks per tile
   constexpr int RW = 32 * RB;
@@ -132,19 +133,28 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
     L = a.Sk;
     off = a.Sk - a.Sq;
   }
+  // key j is allowed for the query at position p iff p - wlft <= j <= p + wrgt
+  // (causal caps wrgt at 0; without a window the bounds are compile-time
+  // constants and the unbounded sides drop out)
+  const int wrgt = WIN ? (CAUSAL ? min(a.wr, 0) : a.wr) : 0;
+  const int wlft = WIN ? a.wl : 0;
   const int q0 = qt * BM;
   const int rows_end = min(q0 + BM, a.Sq);
-  int kend = L;
-  if (CAUSAL) kend = max(0, min(L, off + rows_end));
-  const int ntiles = (kend + BN - 1) / BN;
+  int kend = L, kbeg = 0;
+  if (WIN || CAUSAL) kend = max(0, min(L, off + rows_end + wrgt));
+  if (WIN) kbeg = min(kend, max(0, off + q0 - wlft));
+  const int t_lo = WIN ? kbeg / BN : 0;              // first key tile of the unit
+  const int ntiles = max(0, (kend + BN - 1) / BN - t_lo);
   const int nit = (ntiles + NS - 1) / NS;
 
   const int wr0 = q0 + rw * RW;
   const int wr1 = min(wr0 + RW, a.Sq);
   const bool wave_active = wr0 < a.Sq;
   const int pmin = off + wr0;
-  int wkend = L;
-  if (CAUSAL) wkend = max(0, min(L, off + wr1));
+  const int pmax = off + wr1 - 1;
+  int wkend = L, wkbeg = 0;
+  if (WIN || CAUSAL) wkend = max(0, min(L, pmax + wrgt + 1));
+  if (WIN) wkbeg = max(0, pmin - wlft);
 
   const uint16_t* qbase = a.q + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh;
   const uint16_t* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
@@ -217,7 +227,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
   const float c = FASTC ? a.c : 1.f;
   const float cpre = a.c;   // general path: scores are multiplied by c first
 
-  if (nit > 0 && g < ntiles) issue(g, 0);
+  if (nit > 0 && g < ntiles) issue(t_lo + g, 0);
 
   const int grp = lane >> 4;
   const int tr_t = (lane & 15) >> 2;
@@ -225,13 +235,14 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
 
   for (int it = 0; it < nit; ++it) {
     const int s = it & 1;
-    const int t = it * NS + g;
+    const int tr = it * NS + g;                  // tile index inside the unit
+    const int t = t_lo + tr;
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this lane's DMA for stage s landed
     __syncthreads();                      // ... and every lane's; stage s^1 is free again
-    if (it + 1 < nit && t + NS < ntiles) issue(t + NS, s ^ 1);
+    if (it + 1 < nit && tr + NS < ntiles) issue(t + NS, s ^ 1);
 
     const int key0 = t * BN;
-    if (t >= ntiles || !wave_active || key0 >= wkend) continue;
+    if (tr >= ntiles || !wave_active || key0 >= wkend || (WIN && key0 + BN <= wkbeg)) continue;
     const uint16_t* kt = lds16 + (g * 2 + s) * STAGE;
     const uint16_t* vt = kt + KT;
 
@@ -240,7 +251,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
     bool blk_on[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      blk_on[kb] = key0 + kb * 32 < wkend;
+      blk_on[kb] = key0 + kb * 32 < wkend && (!WIN || key0 + kb * 32 + 32 > wkbeg);
       if (blk_on[kb]) {
         const int krow = kb * 32 + key_perm(lane & 31);
         const uint16_t* kr = kt + krow * DQK;
@@ -259,7 +270,8 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
     }
 
     // ---- mask, row max, lazy rescale, P
-    const bool need_mask = (key0 + BN > L) || (CAUSAL && key0 + BN - 1 > pmin) || !blk_on[NKB - 1];
+    const bool need_mask = (key0 + BN > L) || ((WIN || CAUSAL) && key0 + BN - 1 > pmin + wrgt) ||
+                           (WIN && key0 < pmax - wlft) || (WIN && !blk_on[0]) || !blk_on[NKB - 1];
     u32x4 pf[RB][NKB][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -277,7 +289,8 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = key0 + kb * 32 + 16 * (r >> 3) + 8 * hh + (r & 7);
-            const bool ok = blk_on[kb] && key < L && (!CAUSAL || key <= qpos);
+            const bool ok = blk_on[kb] && key < L && (!(WIN || CAUSAL) || key <= qpos + wrgt) &&
+                            (!WIN || key >= qpos - wlft);
             sc[rb][kb][r] = ok ? sc[rb][kb][r] : -__builtin_inff();
           }
       }
@@ -444,7 +457,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
 }
 
 // ---------------------------------------------------------------- launchers
-template <class T, int DQK, int DV, bool CAUSAL, int RB, int NR, int NS, int BN, bool PAIR, int MINW>
+template <class T, int DQK, int DV, bool CAUSAL, bool WIN, int RB, int NR, int NS, int BN, bool PAIR, int MINW>
 static hipError_t launch_cfg(const AttnArgs& a0, bool fastc, hipStream_t st) {
   AttnArgs a = a0;
   constexpr int BM = NR * 32 * RB;
@@ -454,34 +467,39 @@ static hipError_t launch_cfg(const AttnArgs& a0, bool fastc, hipStream_t st) {
   a.xcd_remap = (units % 8 == 0) ? 1 : 0;
   const dim3 grid((unsigned)units), block(64 * NR * NS);
   if (fastc)
-    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, RB, NR, NS, BN, PAIR, true, MINW>), grid, block,
-                       0, st, a);
+    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, WIN, RB, NR, NS, BN, PAIR, true, MINW>), grid,
+                       block, 0, st, a);
   else
-    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, RB, NR, NS, BN, PAIR, false, MINW>), grid, block,
-                       0, st, a);
+    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, WIN, RB, NR, NS, BN, PAIR, false, MINW>), grid,
+                       block, 0, st, a);
   return hipGetLastError();
 }
 
 // Rows per workgroup and key splits per head dimension: small problems get
 // key-split groups so that every CU runs several waves.
-template <class T, int DQK, int DV, bool CAUSAL>
+template <class T, int DQK, int DV, bool CAUSAL, bool WIN>
 static hipError_t launch_dims(const AttnArgs& a, bool fastc, hipStream_t st) {
   const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
   if constexpr (DQK <= 16) {
-    return launch_cfg<T, DQK, DV, CAUSAL, 1, 4, 1, 64, false, 2>(a, fastc, st);
+    return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 1, 64, false, 2>(a, fastc, st);
   } else if constexpr (DQK <= 64) {
-    if (CAUSAL) return launch_cfg<T, DQK, DV, CAUSAL, 1, 2, 4, 32, true, 2>(a, fastc, st);
-    if (rows <= 256 * 256) return launch_cfg<T, DQK, DV, CAUSAL, 1, 4, 2, 64, false, 2>(a, fastc, st);
-    return launch_cfg<T, DQK, DV, CAUSAL, 2, 2, 2, 64, false, 2>(a, fastc, st);
+    if (CAUSAL) return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 2, 4, 32, true, 2>(a, fastc, st);
+    if (rows <= 256 * 256) return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 2, 64, false, 2>(a, fastc, st);
+    return launch_cfg<T, DQK, DV, CAUSAL, WIN, 2, 2, 2, 64, false, 2>(a, fastc, st);
   } else {
     // one query block per wave keeps two waves per SIMD at these head sizes
-    return launch_cfg<T, DQK, DV, CAUSAL, 1, 4, 1, 64, false, 2>(a, fastc, st);
+    return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 1, 64, false, 2>(a, fastc, st);
   }
 }
 
 template <class T, int DQK, int DV>
 static hipError_t launch_tile_c(const AttnArgs& a, bool causal, bool fastc, hipStream_t st) {
-  return causal ? launch_dims<T, DQK, DV, true>(a, fastc, st) : launch_dims<T, DQK, DV, false>(a, fastc, st);
+  const bool win = a.wl < kNoWindow || a.wr < kNoWindow;
+  if (win)
+    return causal ? launch_dims<T, DQK, DV, true, true>(a, fastc, st)
+                  : launch_dims<T, DQK, DV, false, true>(a, fastc, st);
+  return causal ? launch_dims<T, DQK, DV, true, false>(a, fastc, st)
+                : launch_dims<T, DQK, DV, false, false>(a, fastc, st);
 }
 
 template <class T>

@@ -96,6 +96,13 @@ typedef struct attn_tensor4 {
  * causal: key j is allowed for query i iff j <= i + Sk - Sq (bottom-right
  *     alignment, i.e. j <= i when Sq == Sk); a row with no allowed key
  *     produces zeros.
+ * window_left, window_right: local (sliding-window) attention, the
+ *     window_size=(left, right) of the skill page "Flash Attention - Fast
+ *     Memory-Efficient Attention" (Workflow 2, Step 3).  With query i at
+ *     position p = i + Sk - Sq, key j is allowed only if p - window_left <=
+ *     j <= p + window_right; -1 leaves that side unbounded (-1, -1 = no
+ *     window).  Combined with causal by intersection.  Values < -1 are
+ *     rejected (ATTN_E_SHAPE).
  */
 typedef struct attn_fwd_params {
   attn_dtype dtype;
@@ -104,6 +111,7 @@ typedef struct attn_fwd_params {
   float* lse;
   int causal;
   float softmax_scale;
+  int window_left, window_right;
 } attn_fwd_params;
 
 int attn_fwd(const attn_fwd_params* p, void* stream);
@@ -162,6 +170,7 @@ typedef struct attn_kvcache_params {
   void* workspace;
   size_t workspace_bytes;
   int num_splits;
+  int window_left, window_right;   /* as in attn_fwd_params, on absolute positions */
 } attn_kvcache_params;
 
 size_t attn_fwd_kvcache_workspace_size(const attn_kvcache_params* p);
@@ -197,7 +206,7 @@ int attn_validate_fwd(const attn_fwd_params* p);
 int attn_validate_kvcache(const attn_kvcache_params* p);
 int attn_validate_rope(const attn_rope_params* p);
 const char* attn_last_error(void);
-int attn_abi_version(void);  /* 1 */
+int attn_abi_version(void);  /* 2 */
 
 #ifdef __cplusplus
 }

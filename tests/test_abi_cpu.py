@@ -34,7 +34,7 @@ def test_header_functions_are_all_exported():
     lib = ctypes.CDLL(E.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert E.lib().attn_abi_version() == 1
+    assert E.lib().attn_abi_version() == 2
 
 
 def test_single_hip_runtime_in_process():
@@ -79,6 +79,12 @@ def test_validate_fwd_ok_and_errors():
     p, keep = _fwd()
     p.dtype = 7
     assert _code_fwd(p) == -3
+    p, keep = _fwd()
+    p.window_left = -2
+    assert _code_fwd(p) == -2
+    p, keep = _fwd()
+    p.window_left, p.window_right = 0, 0
+    assert _code_fwd(p) == 0
     # empty problems are valid no-ops
     p, keep = _fwd(Sq=0)
     assert _code_fwd(p) == 0
