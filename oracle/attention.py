@@ -85,3 +85,36 @@ def attention_ref(q, k, v, *, causal: bool = False, softmax_scale=None,
             out[b, :, h, :] = o
             lse[b, h, has] = m[has] + np.log(l[has])
     return out, lse
+
+
+def attention_varlen_ref(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: bool = False,
+                         softmax_scale=None, window=(-1, -1)):
+    """Attention over packed variable-length sequences, fp64.
+
+    Reading (the pages only name a variable-length mode, for the rotary kernel,
+    and say decode uses the batched layout): sequence b owns query rows
+    ``cu_seqlens_q[b] : cu_seqlens_q[b+1]`` of q [total_q, Hq, Dqk] and key rows
+    ``cu_seqlens_k[b] : cu_seqlens_k[b+1]`` of k [total_k, Hkv, Dqk] and
+    v [total_k, Hkv, Dv]; each sequence is attended exactly like one batch
+    element of ``attention_ref`` (same masks, positions counted inside the
+    sequence).  Returns (out [total_q, Hq, Dv], lse [Hq, total_q]).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    cq = [int(x) for x in cu_seqlens_q]
+    ck = [int(x) for x in cu_seqlens_k]
+    assert len(cq) == len(ck) and cq[0] == 0 and ck[0] == 0
+    total_q, Hq, _ = q.shape
+    Dv = v.shape[-1]
+    out = np.zeros((total_q, Hq, Dv), np.float64)
+    lse = np.full((Hq, total_q), -np.inf, np.float64)
+    for b in range(len(cq) - 1):
+        q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        if q1 == q0:
+            continue
+        o, l = attention_ref(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], causal=causal,
+                             softmax_scale=softmax_scale, window=window)
+        out[q0:q1] = o[0]
+        lse[:, q0:q1] = l[0]
+    return out, lse

@@ -16,8 +16,8 @@ import torch
 from scipy.special import logsumexp
 
 import workloads as W
-from oracle import (attention_ref, bits_to_f64, dtype_bits, f32_to_bf16_rne_bits,
-                    kvcache_ref, rope_ref, round_to_dtype, to_f64)
+from oracle import (attention_ref, attention_varlen_ref, bits_to_f64, dtype_bits,
+                    f32_to_bf16_rne_bits, kvcache_ref, rope_ref, round_to_dtype, to_f64)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 rng = np.random.default_rng(1234)
@@ -230,6 +230,48 @@ def test_window_uniform_weights_average_the_window():
     for i in range(7):
         lo, hi = max(0, i - left), min(7, i + right + 1)
         assert np.allclose(out[0, i, 0], v[0, lo:hi, 0].mean(axis=0), rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- packed sequences
+
+def _pack(lens_q, lens_k, Hq, Hkv, Dqk, Dv, seed):
+    rng = np.random.default_rng(seed)
+    cq = np.concatenate([[0], np.cumsum(lens_q)]).astype(int)
+    ck = np.concatenate([[0], np.cumsum(lens_k)]).astype(int)
+    q = rng.standard_normal((cq[-1], Hq, Dqk))
+    k = rng.standard_normal((ck[-1], Hkv, Dqk))
+    v = rng.standard_normal((ck[-1], Hkv, Dv))
+    return q, k, v, cq, ck
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", [(-1, -1), (1, 0)])
+def test_varlen_brute_force_tiny(causal, window):
+    # each packed sequence is attended on its own: brute force per sequence
+    q, k, v, cq, ck = _pack([3, 0, 2, 4], [2, 3, 5, 4], 2, 1, 3, 2, seed=1)
+    out, lse = attention_varlen_ref(q, k, v, cq, ck, causal=causal, softmax_scale=0.6, window=window)
+    for b in range(4):
+        qs, ks = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
+        ref = _brute_attention(q[None, qs], k[None, ks], v[None, ks], causal, 0.6, window=window)
+        assert np.allclose(out[qs], ref[0], rtol=0, atol=1e-12)
+
+
+def test_varlen_equal_lengths_is_the_batched_layout():
+    # B sequences of one length packed back to back = a [B, S, H, D] batch
+    B, S, Sk = 3, 5, 7
+    q, k, v, cq, ck = _pack([S] * B, [Sk] * B, 4, 2, 3, 2, seed=2)
+    out, lse = attention_varlen_ref(q, k, v, cq, ck, causal=True, softmax_scale=0.5)
+    bo, bl = attention_ref(q.reshape(B, S, 4, 3), k.reshape(B, Sk, 2, 3), v.reshape(B, Sk, 2, 2),
+                           causal=True, softmax_scale=0.5)
+    assert np.array_equal(out, bo.reshape(B * S, 4, 2))
+    assert np.array_equal(lse, bl.transpose(1, 0, 2).reshape(4, B * S))
+
+
+def test_varlen_empty_key_sequence_gives_zero_rows():
+    q, k, v, cq, ck = _pack([2, 3], [0, 4], 1, 1, 2, 2, seed=3)
+    out, lse = attention_varlen_ref(q, k, v, cq, ck)
+    assert np.all(out[:2] == 0) and np.all(np.isneginf(lse[:, :2]))
+    assert np.all(np.isfinite(lse[:, 2:]))
 
 
 # ---------------------------------------------------------------- rope
