@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
-                    help="comma list of extra workloads to time: decode, chunked, asym, empty "
+                    help="comma list of extra workloads to time: decode, chunked, window, varlen, asym, empty "
                          "(default: all; 'none' times the headline only)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -204,6 +204,34 @@ def main():
                                       "gbs": byt / t / 1e9, "pct_hbm_peak": 100 * byt / t / 1e9 / PEAK_HBM_GBS}
         del calls
         torch.cuda.empty_cache()
+
+    # ---------------- local window: the headline shape with window_size=(256, 256), causal
+    if want("window"):
+        c = W.fwd_d64(True)
+        q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
+        out = torch.empty_like(q)
+        call = E.prepare_fwd(q, k, v, out, True, c.softmax_scale, window_size=(256, 256))
+        t = time_loop([call], K, Wm, torch)
+        fl = W.fwd_flops(2, 2048, 2048, 8, 64, 64, True, window=(256, 256))
+        results["fwd_b2h8s2048d64_causal_window256"] = {
+            "us": t * 1e6, "gflop": fl / 1e9, "tflops": fl / t / 1e12,
+            "pct_mfma_peak": 100 * fl / t / 1e12 / PEAK_TFLOPS}
+        del call, q, k, v, out, c
+
+    # ---------------- packed sequences: the headline token budget (2 x 2048) as 7 seeded lengths
+    if want("varlen"):
+        lens = W.packed_lengths(4096, 7, seed=0)
+        c = W.random_varlen(lens, lens, 8, 8, 64, 64, "fp16", True, seed=0)
+        q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
+        cq, ck = c.cu_seqlens_q.to(dev), c.cu_seqlens_k.to(dev)
+        out = torch.empty_like(q)
+        call = E.prepare_varlen(q, k, v, out, cq, ck, c.max_seqlen_q, True, 0.125)
+        t = time_loop([call], K, Wm, torch)
+        fl = sum(W.fwd_flops(1, n, n, 8, 64, 64, True) for n in lens)
+        results["varlen_7seq_4096tok_h8d64_causal"] = {
+            "us": t * 1e6, "gflop": fl / 1e9, "tflops": fl / t / 1e12,
+            "pct_mfma_peak": 100 * fl / t / 1e12 / PEAK_TFLOPS, "lengths": lens}
+        del call, q, k, v, out, c
 
     # ---------------- asymmetric head dims: B=2 H=16 S=4096 Dqk=192 Dv=128 bf16 causal
     if want("asym"):

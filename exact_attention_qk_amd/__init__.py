@@ -30,9 +30,9 @@ _lib = ctypes.CDLL(LIB_PATH)
 ATTN_OK = 0
 ERRORS = {-1: "ATTN_E_NULL", -2: "ATTN_E_SHAPE", -3: "ATTN_E_UNSUPPORTED", -4: "ATTN_E_ALIGN",
           -5: "ATTN_E_WORKSPACE", -6: "ATTN_E_OVERFLOW", -7: "ATTN_E_HIP"}
-EXPORTED = ["attn_fwd", "attn_fwd_kvcache", "attn_fwd_kvcache_workspace_size", "rope_apply",
-            "attn_validate_fwd", "attn_validate_kvcache", "attn_validate_rope",
-            "attn_last_error", "attn_abi_version"]
+EXPORTED = ["attn_fwd", "attn_fwd_varlen", "attn_fwd_kvcache", "attn_fwd_kvcache_workspace_size",
+            "rope_apply", "attn_validate_fwd", "attn_validate_varlen", "attn_validate_kvcache",
+            "attn_validate_rope", "attn_last_error", "attn_abi_version"]
 
 
 class AttnError(RuntimeError):
@@ -53,6 +53,16 @@ class FwdParams(ctypes.Structure):
                 ("q", Tensor4), ("k", Tensor4), ("v", Tensor4), ("out", Tensor4),
                 ("lse", ctypes.c_void_p), ("causal", ctypes.c_int),
                 ("softmax_scale", ctypes.c_float),
+                ("window_left", ctypes.c_int), ("window_right", ctypes.c_int)]
+
+
+class VarlenParams(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("B", ctypes.c_int), ("total_q", ctypes.c_int),
+                ("total_k", ctypes.c_int), ("max_seqlen_q", ctypes.c_int), ("Hq", ctypes.c_int),
+                ("Hkv", ctypes.c_int), ("Dqk", ctypes.c_int), ("Dv", ctypes.c_int),
+                ("q", Tensor4), ("k", Tensor4), ("v", Tensor4), ("out", Tensor4),
+                ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p), ("causal", ctypes.c_int), ("softmax_scale", ctypes.c_float),
                 ("window_left", ctypes.c_int), ("window_right", ctypes.c_int)]
 
 
@@ -82,6 +92,8 @@ class RopeParams(ctypes.Structure):
 
 
 _lib.attn_fwd.argtypes = [ctypes.POINTER(FwdParams), ctypes.c_void_p]
+_lib.attn_fwd_varlen.argtypes = [ctypes.POINTER(VarlenParams), ctypes.c_void_p]
+_lib.attn_validate_varlen.argtypes = [ctypes.POINTER(VarlenParams)]
 _lib.attn_fwd_kvcache.argtypes = [ctypes.POINTER(KVCacheParams), ctypes.c_void_p]
 _lib.attn_fwd_kvcache_workspace_size.argtypes = [ctypes.POINTER(KVCacheParams)]
 _lib.attn_fwd_kvcache_workspace_size.restype = ctypes.c_size_t
@@ -90,8 +102,8 @@ _lib.attn_validate_fwd.argtypes = [ctypes.POINTER(FwdParams)]
 _lib.attn_validate_kvcache.argtypes = [ctypes.POINTER(KVCacheParams)]
 _lib.attn_validate_rope.argtypes = [ctypes.POINTER(RopeParams)]
 _lib.attn_last_error.restype = ctypes.c_char_p
-for _n in ("attn_fwd", "attn_fwd_kvcache", "rope_apply", "attn_validate_fwd",
-           "attn_validate_kvcache", "attn_validate_rope", "attn_abi_version"):
+for _n in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_kvcache", "rope_apply", "attn_validate_fwd",
+           "attn_validate_varlen", "attn_validate_kvcache", "attn_validate_rope", "attn_abi_version"):
     getattr(_lib, _n).restype = ctypes.c_int
 
 _DT = {torch.float16: 0, torch.bfloat16: 1}
@@ -153,6 +165,52 @@ def attn_fwd(q, k, v, causal=False, softmax_scale=None, out=None, return_lse=Fal
     p = fwd_params(q, k, v, out, causal, softmax_scale, lse, window_size)
     _check(_lib.attn_fwd(ctypes.byref(p), _stream(q)))
     return (out, lse) if return_lse else out
+
+
+# ---------------------------------------------------------------- packed sequences
+
+def _t3(x):
+    """A packed [total, H, D] tensor as the ABI's tensor block (batch stride unused)."""
+    if x is None:
+        return Tensor4(None, 0, 0, 0)
+    assert x.dim() == 3 and x.stride(2) == 1
+    return Tensor4(x.data_ptr(), 0, x.stride(0), x.stride(1))
+
+
+def varlen_params(q, k, v, out, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal=False,
+                  softmax_scale=None, lse=None, window_size=(-1, -1)):
+    total_q, Hq, Dqk = q.shape
+    total_k, Hkv, Dv = k.shape[0], k.shape[1], v.shape[2]
+    for cu in (cu_seqlens_q, cu_seqlens_k):
+        assert cu.dtype == torch.int32 and cu.is_contiguous() and cu.is_cuda == q.is_cuda
+    B = cu_seqlens_q.numel() - 1
+    return VarlenParams(_dtype(q), B, total_q, total_k, int(max_seqlen_q), Hq, Hkv, Dqk, Dv,
+                        _t3(q), _t3(k), _t3(v), _t3(out), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+                        lse.data_ptr() if lse is not None else None, int(bool(causal)),
+                        _scale(softmax_scale), int(window_size[0]), int(window_size[1]))
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal=False,
+                    softmax_scale=None, out=None, return_lse=False, window_size=(-1, -1)):
+    """Attention over packed sequences: q [total_q, Hq, Dqk], k/v [total_k, Hkv, D*],
+    cu_seqlens_* int32 [B+1] on the device -> out [total_q, Hq, Dv] (lse [Hq, total_q])."""
+    total_q, Hq, _ = q.shape
+    Dv = v.shape[2]
+    if out is None:
+        out = torch.empty((total_q, Hq, Dv), dtype=q.dtype, device=q.device)
+    lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device) if return_lse else None
+    p = varlen_params(q, k, v, out, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal, softmax_scale,
+                      lse, window_size)
+    _check(_lib.attn_fwd_varlen(ctypes.byref(p), _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+def prepare_varlen(q, k, v, out, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal=False,
+                   softmax_scale=None, lse=None, window_size=(-1, -1)):
+    p = varlen_params(q, k, v, out, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal, softmax_scale,
+                      lse, window_size)
+    return PreparedCall(_lib.attn_fwd_varlen, p, _stream(q),
+                        (q, k, v, out, cu_seqlens_q, cu_seqlens_k, lse))
 
 
 # ---------------------------------------------------------------- kvcache
@@ -277,6 +335,8 @@ def prepare_kvcache(q, k_cache, v_cache, k, v, out, *, rotary_cos=None, rotary_s
                          lse, ws))
 
 
-__all__ = ["PreparedCall", "prepare_fwd", "prepare_kvcache", "attn_fwd", "attn_fwd_kvcache", "rope_apply", "kvcache_workspace_size", "AttnError",
-           "FwdParams", "KVCacheParams", "RopeParams", "Tensor4", "fwd_params", "kvcache_params",
+__all__ = ["PreparedCall", "prepare_fwd", "prepare_varlen", "prepare_kvcache", "attn_fwd", "attn_fwd_varlen",
+           "attn_fwd_kvcache", "rope_apply", "kvcache_workspace_size", "AttnError",
+           "FwdParams", "VarlenParams", "KVCacheParams", "RopeParams", "Tensor4", "fwd_params",
+           "varlen_params", "kvcache_params",
            "rope_params", "lib", "EXPORTED", "LIB_PATH"]

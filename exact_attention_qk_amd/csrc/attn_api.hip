@@ -258,6 +258,32 @@ int hip_fail(hipError_t e, const char* what) {
 
 }  // namespace
 
+int validate_varlen(const attn_varlen_params* p) {
+  if (!p) return fail(ATTN_E_NULL, "params pointer is NULL");
+  int e;
+  if ((e = check_dtype(p->dtype))) return e;
+  if (p->B < 0 || p->total_q < 0 || p->total_k < 0 || p->max_seqlen_q < 0 || p->Hq < 1 || p->Hkv < 1)
+    return fail(ATTN_E_SHAPE, "sizes must satisfy B, total_q, total_k, max_seqlen_q >= 0 and Hq, Hkv >= 1");
+  if (p->total_q >= attn::kNoWindow || p->total_k >= attn::kNoWindow)
+    return fail(ATTN_E_SHAPE, "sequence lengths must be below 2^29");
+  if (p->Hq % p->Hkv)
+    return fail(ATTN_E_SHAPE, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+  if (!dims_supported(p->Dqk, p->Dv))
+    return fail(ATTN_E_UNSUPPORTED, "(Dqk, Dv) = (%d, %d) is not one of (16,16), (64,64), (128,128), (192,128)",
+                p->Dqk, p->Dv);
+  if (p->window_left < -1 || p->window_right < -1)
+    return fail(ATTN_E_SHAPE, "window (%d, %d): each side must be >= -1", p->window_left, p->window_right);
+  if (p->B == 0 || p->total_q == 0) return ok();
+  if (!p->cu_seqlens_q || !p->cu_seqlens_k) return fail(ATTN_E_NULL, "cu_seqlens_q / cu_seqlens_k is NULL");
+  if ((e = check_tensor(p->q, "q"))) return e;
+  if (p->total_k > 0) {
+    if ((e = check_tensor(p->k, "k"))) return e;
+    if ((e = check_tensor(p->v, "v"))) return e;
+  }
+  if ((e = check_tensor(p->out, "out"))) return e;
+  return ok();
+}
+
 extern "C" {
 
 int attn_abi_version(void) { return 2; }
@@ -266,6 +292,7 @@ const char* attn_last_error(void) { return g_err.c_str(); }
 
 int attn_validate_fwd(const attn_fwd_params* p) { return validate_fwd(p); }
 int attn_validate_kvcache(const attn_kvcache_params* p) { return validate_kvcache(p); }
+int attn_validate_varlen(const attn_varlen_params* p) { return validate_varlen(p); }
 int attn_validate_rope(const attn_rope_params* p) { return validate_rope(p); }
 
 int attn_fwd(const attn_fwd_params* p, void* stream) {
@@ -275,6 +302,7 @@ int attn_fwd(const attn_fwd_params* p, void* stream) {
   attn::AttnArgs a = base_args();
   set_q(a, p->q); set_k(a, p->k); set_v(a, p->v); set_o(a, p->out);
   a.lse = p->lse;
+  a.lse_sb = (int64_t)p->Hq * p->Sq; a.lse_sh = p->Sq;
   a.B = p->B; a.Sq = p->Sq; a.Sk = p->Sk; a.Hq = p->Hq; a.Hkv = p->Hkv; a.group = p->Hq / p->Hkv;
   a.kvcache = 0;
   a.causal = p->causal ? 1 : 0;
@@ -283,6 +311,48 @@ int attn_fwd(const attn_fwd_params* p, void* stream) {
   hipError_t he = attn::run_tile_attn(a, p->dtype == ATTN_DTYPE_BF16, p->Dqk, p->Dv, p->causal != 0,
                                       static_cast<hipStream_t>(stream));
   if (he != hipSuccess) return hip_fail(he, "attn_fwd launch");
+  return ok();
+}
+
+int attn_fwd_varlen(const attn_varlen_params* p, void* stream) {
+  int e = validate_varlen(p);
+  if (e) return e;
+  if (p->B == 0 || p->total_q == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (env_check()) {
+    std::vector<int32_t> cq(p->B + 1), ck(p->B + 1);
+    hipError_t he = hipMemcpyAsync(cq.data(), p->cu_seqlens_q, sizeof(int32_t) * cq.size(),
+                                   hipMemcpyDeviceToHost, st);
+    if (he == hipSuccess)
+      he = hipMemcpyAsync(ck.data(), p->cu_seqlens_k, sizeof(int32_t) * ck.size(), hipMemcpyDeviceToHost, st);
+    if (he == hipSuccess) he = hipStreamSynchronize(st);
+    if (he != hipSuccess) return hip_fail(he, "ATTN_CHECK copy of cu_seqlens");
+    if (cq[0] != 0 || ck[0] != 0 || cq[p->B] != p->total_q || ck[p->B] != p->total_k)
+      return fail(ATTN_E_SHAPE, "cu_seqlens must start at 0 and end at total_q / total_k");
+    for (int b = 0; b < p->B; ++b) {
+      if (cq[b + 1] < cq[b] || ck[b + 1] < ck[b])
+        return fail(ATTN_E_SHAPE, "cu_seqlens must be non-decreasing (sequence %d)", b);
+      if (cq[b + 1] - cq[b] > p->max_seqlen_q)
+        return fail(ATTN_E_SHAPE, "sequence %d has %d query rows > max_seqlen_q %d", b, cq[b + 1] - cq[b],
+                    p->max_seqlen_q);
+    }
+  }
+  attn::AttnArgs a = base_args();
+  set_q(a, p->q); set_k(a, p->k); set_v(a, p->v); set_o(a, p->out);
+  a.q_sb = a.k_sb = a.v_sb = a.o_sb = 0;
+  a.lse = p->lse;
+  a.lse_sb = 0; a.lse_sh = p->total_q;
+  a.varlen = 1;
+  a.cu_q = p->cu_seqlens_q;
+  a.cu_k = p->cu_seqlens_k;
+  a.B = p->B; a.Sq = p->max_seqlen_q; a.Sk = 0; a.Hq = p->Hq; a.Hkv = p->Hkv; a.group = p->Hq / p->Hkv;
+  a.kvcache = 0;
+  a.causal = p->causal ? 1 : 0;
+  set_window(a, p->window_left, p->window_right);
+  a.c = resolve_c(p->softmax_scale, p->Dqk);
+  if (p->max_seqlen_q == 0) return ok();
+  hipError_t he = attn::run_tile_attn(a, p->dtype == ATTN_DTYPE_BF16, p->Dqk, p->Dv, p->causal != 0, st);
+  if (he != hipSuccess) return hip_fail(he, "attn_fwd_varlen launch");
   return ok();
 }
 
@@ -367,6 +437,7 @@ int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream) {
   }
   set_k(a, p->k_cache); set_v(a, p->v_cache); set_o(a, p->out);
   a.lse = p->lse;
+  a.lse_sb = (int64_t)p->Hq * p->Sq; a.lse_sh = p->Sq;
   a.seqlens = p->cache_seqlens;
   a.seqlen_scalar = p->cache_seqlens_scalar;
   a.B = p->B; a.Sq = p->Sq; a.Sk = p->capacity; a.Hq = p->Hq; a.Hkv = p->Hkv; a.group = p->Hq / p->Hkv;

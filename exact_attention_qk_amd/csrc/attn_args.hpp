@@ -11,7 +11,11 @@ struct AttnArgs {
   const uint16_t* k;  int64_t k_sb, k_ss, k_sh;
   const uint16_t* v;  int64_t v_sb, v_ss, v_sh;
   uint16_t* out;      int64_t o_sb, o_ss, o_sh;
-  float* lse;                 // [B, Hq, Sq] or null
+  float* lse;                 // [B, Hq, Sq] or null; element (b, h, i) at b*lse_sb + h*lse_sh + i
+  int64_t lse_sb, lse_sh;     // (packed sequences: 0 and total_q, i counted over the whole pack)
+  int varlen;                 // 1: packed sequences, bounds from cu_q / cu_k (device [B+1])
+  const int32_t* cu_q;
+  const int32_t* cu_k;
   const int32_t* seqlens;     // per-batch cache_seqlens (kvcache mode) or null
   int seqlen_scalar;          // cache_seqlens for every batch when seqlens is null
   int B, Sq, Sk, Hq, Hkv, group, Snew;

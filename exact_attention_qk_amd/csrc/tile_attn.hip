@@ -120,12 +120,23 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
   const int hq = bh - b * a.Hq;
   const int hkv = hq / a.group;
   const int nslots = (PAIR && nqt - 1 - pu != pu) ? 2 : 1;
+  // packed variable-length batches: sequence b owns query rows [qst, qst + Sqb)
+  // and key rows from kst on; the grid covers the longest query sequence
+  int Sqb = a.Sq, qst = 0, kst = 0;
+  if (a.varlen) {
+    qst = a.cu_q[b];
+    Sqb = a.cu_q[b + 1] - qst;
+    kst = a.cu_k[b];
+  }
   for (int slot = 0; slot < nslots; ++slot) {
   int qt = pu;
   if (CAUSAL) qt = (PAIR && slot == 1) ? pu : nqt - 1 - pu;   // heavy tiles first
 
   int L, off;
-  if (a.kvcache) {
+  if (a.varlen) {
+    L = a.cu_k[b + 1] - kst;
+    off = L - Sqb;
+  } else if (a.kvcache) {
     const int cb = a.seqlens ? a.seqlens[b] : a.seqlen_scalar;
     L = cb + a.Snew;
     off = cb;
@@ -139,7 +150,8 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
   const int wrgt = WIN ? (CAUSAL ? min(a.wr, 0) : a.wr) : 0;
   const int wlft = WIN ? a.wl : 0;
   const int q0 = qt * BM;
-  const int rows_end = min(q0 + BM, a.Sq);
+  if (q0 >= Sqb) continue;   // a query tile past this sequence's end (uniform)
+  const int rows_end = min(q0 + BM, Sqb);
   int kend = L, kbeg = 0;
   if (WIN || CAUSAL) kend = max(0, min(L, off + rows_end + wrgt));
   if (WIN) kbeg = min(kend, max(0, off + q0 - wlft));
@@ -148,17 +160,17 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
   const int nit = (ntiles + NS - 1) / NS;
 
   const int wr0 = q0 + rw * RW;
-  const int wr1 = min(wr0 + RW, a.Sq);
-  const bool wave_active = wr0 < a.Sq;
+  const int wr1 = min(wr0 + RW, Sqb);
+  const bool wave_active = wr0 < Sqb;
   const int pmin = off + wr0;
   const int pmax = off + wr1 - 1;
   int wkend = L, wkbeg = 0;
   if (WIN || CAUSAL) wkend = max(0, min(L, pmax + wrgt + 1));
   if (WIN) wkbeg = max(0, pmin - wlft);
 
-  const uint16_t* qbase = a.q + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh;
-  const uint16_t* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
-  const uint16_t* vbase = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+  const uint16_t* qbase = a.q + (int64_t)b * a.q_sb + (int64_t)qst * a.q_ss + (int64_t)hq * a.q_sh;
+  const uint16_t* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)kst * a.k_ss + (int64_t)hkv * a.k_sh;
+  const uint16_t* vbase = a.v + (int64_t)b * a.v_sb + (int64_t)kst * a.v_ss + (int64_t)hkv * a.v_sh;
 
   // ---- tile DMA: tile t of this group into stage s.  Each lane's source row
   // and chunk inside a tile do not depend on the tile, so their byte offsets
@@ -208,7 +220,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int qrow = wr0 + rb * 32 + (lane & 31);
-    const int qr = min(qrow, a.Sq - 1);
+    const int qr = min(qrow, Sqb - 1);
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qf[rb][s] = ldg16(qbase + (int64_t)qr * a.q_ss + 16 * s + 8 * hh);
   }
@@ -429,13 +441,13 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
     if (wave_active) {
-      uint16_t* obase = a.out + (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh;
+      uint16_t* obase = a.out + (int64_t)b * a.o_sb + (int64_t)qst * a.o_ss + (int64_t)hq * a.o_sh;
       constexpr int OCH = RW * CV;
 #pragma unroll
       for (int i = 0; i < (OCH + 63) / 64; ++i) {
         const int id = i * 64 + lane;
         const int row = id / CV, ch = id - (id / CV) * CV;
-        if (id < OCH && wr0 + row < a.Sq) {
+        if (id < OCH && wr0 + row < Sqb) {
           const u32x4 val = *reinterpret_cast<const u32x4*>(lds_o + row * OSTR + ch * 8);
           stg16(obase + (int64_t)(wr0 + row) * a.o_ss + ch * 8, val);
         }
@@ -444,8 +456,8 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const int qrow = wr0 + rb * 32 + lane;
-          if (qrow < a.Sq)
-            a.lse[((int64_t)b * a.Hq + hq) * a.Sq + qrow] =
+          if (qrow < Sqb)
+            a.lse[(int64_t)b * a.lse_sb + (int64_t)hq * a.lse_sh + qst + qrow] =
                 lsum[rb] > 0.f ? (m_use[rb] + __log2f(lsum[rb])) * 0.69314718055994531f
                                : -__builtin_inff();
         }

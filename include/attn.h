@@ -116,6 +116,39 @@ typedef struct attn_fwd_params {
 
 int attn_fwd(const attn_fwd_params* p, void* stream);
 
+/* --------------------------------------------------------- attn_fwd_varlen
+ * Packed variable-length sequences (the variable-length mode that
+ * ROCm/flash-attention PR #99 "Added Support for Rotary Positional Embeddings
+ * (both non-fused and fused kernel)" names for its rotary kernel, review
+ * thread on IS_VARLEN; decode keeps the batched layout).  Sequence b owns
+ * query rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) of q and key rows
+ * [cu_seqlens_k[b], cu_seqlens_k[b+1]) of k and v, and is attended exactly
+ * like one batch element of attn_fwd (same causal alignment, window and
+ * empty-row rules, positions counted inside the sequence).
+ * q   [total_q, Hq,  Dqk]   read     (attn_tensor4 with stride_b ignored)
+ * k   [total_k, Hkv, Dqk]   read
+ * v   [total_k, Hkv, Dv ]   read
+ * out [total_q, Hq,  Dv ]   written
+ * lse [Hq, total_q] fp32, contiguous, written when non-NULL.
+ * cu_seqlens_q, cu_seqlens_k: device int32 [B + 1], non-decreasing, starting
+ * at 0 and ending at total_q / total_k.  max_seqlen_q >= every query length
+ * (it sizes the grid).  These device-side preconditions are not checked
+ * unless ATTN_CHECK=1 is set (the call then copies both arrays to the host).
+ */
+typedef struct attn_varlen_params {
+  attn_dtype dtype;
+  int B, total_q, total_k, max_seqlen_q, Hq, Hkv, Dqk, Dv;
+  attn_tensor4 q, k, v, out;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  float* lse;
+  int causal;
+  float softmax_scale;
+  int window_left, window_right;
+} attn_varlen_params;
+
+int attn_fwd_varlen(const attn_varlen_params* p, void* stream);
+
 /* -------------------------------------------------------- attn_fwd_kvcache
  * q       [B, Sq, Hq, Dqk]            read
  * k_cache [B, capacity, Hkv, Dqk]     read; rows [c_b, c_b + Snew) written
@@ -204,6 +237,7 @@ int rope_apply(const attn_rope_params* p, void* stream);
  */
 int attn_validate_fwd(const attn_fwd_params* p);
 int attn_validate_kvcache(const attn_kvcache_params* p);
+int attn_validate_varlen(const attn_varlen_params* p);
 int attn_validate_rope(const attn_rope_params* p);
 const char* attn_last_error(void);
 int attn_abi_version(void);  /* 2 */

@@ -94,6 +94,21 @@ def test_validate_fwd_ok_and_errors():
     assert _code_fwd(p) == 0
 
 
+def test_validate_varlen():
+    q = _t((10, 4, 64))
+    k = _t((12, 2, 64))
+    cu = torch.zeros(3, dtype=torch.int32)
+    p = E.varlen_params(q, k, k, q, cu, cu, 8)
+    assert E.lib().attn_validate_varlen(ctypes.byref(p)) == 0
+    p.cu_seqlens_k = None
+    assert E.lib().attn_validate_varlen(ctypes.byref(p)) == -1
+    p = E.varlen_params(q, k, k, q, cu, cu, 8, window_size=(3, -4))
+    assert E.lib().attn_validate_varlen(ctypes.byref(p)) == -2
+    p = E.varlen_params(q, k, k, q, cu, cu, 8)
+    p.Dqk = p.Dv = 96
+    assert E.lib().attn_validate_varlen(ctypes.byref(p)) == -3
+
+
 def test_binding_rejects_other_dtypes_before_any_launch():
     q = torch.zeros(1, 4, 1, 64)
     with pytest.raises(AttnError):

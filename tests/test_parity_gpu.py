@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import workloads as W
-from oracle import attention_ref, dtype_bits, kvcache_ref, rope_ref, to_f64
+from oracle import attention_ref, attention_varlen_ref, dtype_bits, kvcache_ref, rope_ref, to_f64
 
 pytestmark = pytest.mark.gpu
 TOL = {"fp16": 2e-3, "bf16": 1.5e-2}
@@ -380,6 +380,65 @@ def test_window_wide_equals_no_window_bitwise():
     b = E().attn_fwd(q, k, v, causal=True, window_size=(400, 400))
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- packed sequences
+
+def _varlen_check(case, window=(-1, -1), max_seqlen_q=None):
+    q, k, v = dev(case.q), dev(case.k), dev(case.v)
+    cq, ck = dev(case.cu_seqlens_q), dev(case.cu_seqlens_k)
+    tq, Hq, _ = q.shape
+    buf, out = guarded_empty((tq, Hq, v.shape[2]), q.dtype)
+    _, lse = E().attn_fwd_varlen(q, k, v, cq, ck, max_seqlen_q or case.max_seqlen_q, causal=case.causal,
+                                 softmax_scale=case.softmax_scale, out=out, return_lse=True,
+                                 window_size=window)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf, out.numel())
+    ref, rlse = attention_varlen_ref(to_f64(case.q), to_f64(case.k), to_f64(case.v),
+                                     case.cu_seqlens_q.tolist(), case.cu_seqlens_k.tolist(),
+                                     causal=case.causal, softmax_scale=case.softmax_scale, window=window)
+    err = maxabs(out, ref)
+    assert err <= TOL[case.dtype], "max abs err %.3e" % err
+    l = lse.cpu().double().numpy()
+    fin = np.isfinite(rlse)
+    assert np.array_equal(fin, np.isfinite(l))
+    assert np.max(np.abs(l[fin] - rlse[fin])) < LSE_TOL[case.dtype]
+    return out
+
+
+VARLEN_LENS = ([0, 1, 65, 200, 129, 7], [3, 1, 200, 65, 129, 0])
+
+
+@pytest.mark.parametrize("dqk,dv,dtype", [(64, 64, "fp16"), (128, 128, "bf16"), (192, 128, "bf16"),
+                                          (16, 16, "fp16")])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_ragged(dqk, dv, dtype, causal):
+    # empty, one-row, multi-tile and ragged sequences; Sq != Sk per sequence; a sequence without keys
+    case = W.random_varlen(*VARLEN_LENS, 4, 2, dqk, dv, dtype, causal, seed=dqk + causal)
+    _varlen_check(case)
+
+
+@pytest.mark.parametrize("window", [(0, 0), (37, 5), (-1, 16)])
+def test_varlen_window(window):
+    case = W.random_varlen(*VARLEN_LENS, 4, 2, 64, 64, "fp16", True, seed=41)
+    _varlen_check(case, window=window)
+
+
+def test_varlen_grid_larger_than_needed():
+    # max_seqlen_q above the longest sequence: surplus query tiles do nothing
+    case = W.random_varlen([100, 30], [100, 30], 2, 2, 64, 64, "fp16", True, seed=43)
+    _varlen_check(case, max_seqlen_q=700)
+
+
+def test_varlen_equal_lengths_bitwise_batched():
+    # packed sequences of one length are the batched layout: same kernel, same bits
+    B, S = 3, 300
+    case = W.random_varlen([S] * B, [S] * B, 4, 2, 64, 64, "fp16", True, seed=45)
+    out = _varlen_check(case)
+    q, k, v = dev(case.q).view(B, S, 4, 64), dev(case.k).view(B, S, 2, 64), dev(case.v).view(B, S, 2, 64)
+    ob = E().attn_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ob.view(B * S, 4, 64), out)
 
 
 # ---------------------------------------------------------------- rope_apply

@@ -179,6 +179,40 @@ def random_fwd(B, Sq, Sk, Hq, Hkv, Dqk, Dv, dtype, causal, seed=0,
     return FwdCase("random_fwd", dtype, q, k, v, causal, softmax_scale)
 
 
+@dataclass
+class VarlenCase:
+    """Packed sequences: q [total_q,Hq,Dqk], k/v [total_k,Hkv,D*], cu_seqlens int32 [B+1]."""
+    name: str
+    dtype: str
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    cu_seqlens_q: torch.Tensor
+    cu_seqlens_k: torch.Tensor
+    max_seqlen_q: int
+    causal: bool
+    softmax_scale: float | None = None
+
+
+def random_varlen(lens_q, lens_k, Hq, Hkv, Dqk, Dv, dtype, causal, seed=0) -> VarlenCase:
+    g = torch.Generator().manual_seed(seed)
+    tq, tk = int(sum(lens_q)), int(sum(lens_k))
+    q = _randn(g, (tq, Hq, Dqk), dtype)
+    k = _randn(g, (tk, Hkv, Dqk), dtype)
+    v = _randn(g, (tk, Hkv, Dv), dtype)
+    cq = torch.tensor([0] + list(np.cumsum(lens_q)), dtype=torch.int32)
+    ck = torch.tensor([0] + list(np.cumsum(lens_k)), dtype=torch.int32)
+    return VarlenCase("random_varlen", dtype, q, k, v, cq, ck, int(max(lens_q) if lens_q else 0), causal)
+
+
+def packed_lengths(total, n, seed, min_len=1):
+    """n seeded lengths >= min_len summing to total (a uniform random composition)."""
+    rng = np.random.default_rng(seed)
+    cuts = np.sort(rng.choice(np.arange(1, total - n * (min_len - 1)), n - 1, replace=False))
+    parts = np.diff(np.concatenate([[0], cuts, [total - n * (min_len - 1)]])) + (min_len - 1)
+    return [int(x) for x in parts]
+
+
 def random_kvcache(B, Sq, Hq, Hkv, Dqk, Dv, capacity, dtype, *, snew, seqlens,
                    rotary_dim=0, interleaved=False, causal=True, seed=0,
                    softmax_scale=None, seqlens_as_tensor=True,
@@ -218,12 +252,23 @@ def seqlens_list(cs, B):
 
 # Algorithmic work per workload (what the method must do, independent of tiling).
 
-def fwd_flops(B, Sq, Sk, Hq, Dqk, Dv, causal):
-    """2*(Dqk+Dv) flop per unmasked (query, key) pair; causal keeps key <= query (+Sk-Sq)."""
-    if causal:
-        pairs = sum(max(0, min(Sk, i + 1 + Sk - Sq)) for i in range(Sq))
-    else:
-        pairs = Sq * Sk
+def fwd_flops(B, Sq, Sk, Hq, Dqk, Dv, causal, window=(-1, -1)):
+    """2*(Dqk+Dv) flop per unmasked (query, key) pair.
+
+    Query i sits at position p = i + Sk - Sq; causal keeps keys j <= p and a
+    local window (left, right) keeps p - left <= j <= p + right (-1: unbounded).
+    """
+    left, right = window
+    pairs = 0
+    for i in range(Sq):
+        p = i + Sk - Sq
+        hi = Sk - 1
+        if causal:
+            hi = min(hi, p)
+        if right >= 0:
+            hi = min(hi, p + right)
+        lo = 0 if left < 0 else max(0, p - left)
+        pairs += max(0, hi - lo + 1)
     return 2.0 * (Dqk + Dv) * B * Hq * pairs
 
 
