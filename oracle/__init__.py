@@ -30,9 +30,10 @@ routines, invariants the pages state, and brute force on tiny shapes.
 from .numerics import round_to_dtype, dtype_bits, bits_to_f64, to_f64, f32_to_bf16_rne_bits
 from .attention import attention_ref, attention_varlen_ref
 from .rope import rope_ref
+from .backward import attention_bwd_ref
 from .kvcache import kvcache_ref
 
 __all__ = [
-    "attention_ref", "attention_varlen_ref", "rope_ref", "kvcache_ref", "round_to_dtype", "dtype_bits",
+    "attention_ref", "attention_varlen_ref", "attention_bwd_ref", "rope_ref", "kvcache_ref", "round_to_dtype", "dtype_bits",
     "bits_to_f64", "to_f64", "f32_to_bf16_rne_bits",
 ]

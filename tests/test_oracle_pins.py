@@ -16,7 +16,7 @@ import torch
 from scipy.special import logsumexp
 
 import workloads as W
-from oracle import (attention_ref, attention_varlen_ref, bits_to_f64, dtype_bits,
+from oracle import (attention_bwd_ref, attention_ref, attention_varlen_ref, bits_to_f64, dtype_bits,
                     f32_to_bf16_rne_bits, kvcache_ref, rope_ref, round_to_dtype, to_f64)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -272,6 +272,75 @@ def test_varlen_empty_key_sequence_gives_zero_rows():
     out, lse = attention_varlen_ref(q, k, v, cq, ck)
     assert np.all(out[:2] == 0) and np.all(np.isneginf(lse[:, :2]))
     assert np.all(np.isfinite(lse[:, 2:]))
+
+
+# ---------------------------------------------------------------- gradients
+# flash-attention PR #1604 "Support hdimQK != hdimV backward": dQ, dK, dV with
+# Dqk != Dv.  Pinned to the forward oracle by central differences and to
+# torch's float64 autograd of a plain torch formulation.
+
+def _loss(q, k, v, dout, **kw):
+    out, _ = attention_ref(q, k, v, **kw)
+    return float(np.sum(out * dout))
+
+
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (False, (1, 2)),
+                                           (True, (2, -1))])
+def test_bwd_central_differences(causal, window):
+    B, Sq, Sk, Hq, Hkv, Dqk, Dv = 1, 4, 5, 2, 1, 3, 2
+    q, k, v = _rand_qkv(B, Sq, Sk, Hq, Hkv, Dqk, Dv, seed=21)
+    dout = np.random.default_rng(22).standard_normal((B, Sq, Hq, Dv))
+    kw = dict(causal=causal, softmax_scale=0.7, window=window)
+    dq, dk, dv = attention_bwd_ref(q, k, v, dout, **kw)
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = _loss(args["q"], args["k"], args["v"], dout, **kw)
+            args[name] = xm
+            lm = _loss(args["q"], args["k"], args["v"], dout, **kw)
+            assert abs((lp - lm) / (2 * eps) - g[idx]) < 1e-7, (name, idx)
+
+
+def test_bwd_matches_torch_autograd_float64():
+    B, Sq, Sk, Hq, Hkv, Dqk, Dv = 2, 6, 7, 4, 2, 5, 3
+    q, k, v = _rand_qkv(B, Sq, Sk, Hq, Hkv, Dqk, Dv, seed=23)
+    dout = np.random.default_rng(24).standard_normal((B, Sq, Hq, Dv))
+    dq, dk, dv = attention_bwd_ref(q, k, v, dout, causal=True, softmax_scale=0.4)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    kr = tk.repeat_interleave(Hq // Hkv, dim=2)
+    vr = tv.repeat_interleave(Hq // Hkv, dim=2)
+    s = torch.einsum("bihd,bjhd->bhij", tq, kr) * 0.4
+    mask = torch.ones(Sq, Sk, dtype=torch.bool).tril(Sk - Sq)
+    s = s.masked_fill(~mask, float("-inf"))
+    o = torch.einsum("bhij,bjhd->bihd", torch.softmax(s, dim=-1), vr)
+    o.backward(torch.tensor(dout))
+    assert np.allclose(tq.grad.numpy(), dq, rtol=0, atol=1e-12)
+    assert np.allclose(tk.grad.numpy(), dk, rtol=0, atol=1e-12)
+    assert np.allclose(tv.grad.numpy(), dv, rtol=0, atol=1e-12)
+
+
+def test_bwd_one_key_closed_form():
+    # one key: P = 1 for every row, so dV = sum of dO rows and dQ = dK = 0
+    q, k, v = _rand_qkv(1, 3, 1, 2, 2, 4, 3, seed=25)
+    dout = np.random.default_rng(26).standard_normal((1, 3, 2, 3))
+    dq, dk, dv = attention_bwd_ref(q, k, v, dout)
+    assert np.allclose(dv[0, 0], dout[0].sum(axis=0), rtol=0, atol=1e-14)
+    assert np.all(np.abs(dq) < 1e-15) and np.all(np.abs(dk) < 1e-15)
+
+
+def test_bwd_gqa_is_sum_over_repeated_heads():
+    q, k, v = _rand_qkv(1, 5, 6, 4, 2, 3, 2, seed=27)
+    dout = np.random.default_rng(28).standard_normal((1, 5, 4, 2))
+    dq, dk, dv = attention_bwd_ref(q, k, v, dout, causal=True)
+    rq, rk, rv = attention_bwd_ref(q, np.repeat(k, 2, axis=2), np.repeat(v, 2, axis=2), dout, causal=True)
+    assert np.allclose(dq, rq, rtol=0, atol=1e-13)
+    assert np.allclose(dk, rk[:, :, 0::2] + rk[:, :, 1::2], rtol=0, atol=1e-13)
+    assert np.allclose(dv, rv[:, :, 0::2] + rv[:, :, 1::2], rtol=0, atol=1e-13)
 
 
 # ---------------------------------------------------------------- rope
