@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
-                    help="comma list of extra workloads to time: decode, chunked, window, varlen, asym, empty "
+                    help="comma list of extra workloads to time: decode, chunked, window, bwd, varlen, asym, empty "
                          "(default: all; 'none' times the headline only)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -217,6 +217,23 @@ def main():
             "us": t * 1e6, "gflop": fl / 1e9, "tflops": fl / t / 1e12,
             "pct_mfma_peak": 100 * fl / t / 1e12 / PEAK_TFLOPS}
         del call, q, k, v, out, c
+
+    # ---------------- gradients on the headline shape (dq, dk, dv from dO), non-causal and causal
+    if want("bwd"):
+        for causal in (False, True):
+            c = W.fwd_d64(causal)
+            q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
+            g = torch.Generator().manual_seed(1)
+            dout = torch.randn(q.shape, generator=g).to(q.dtype).to(dev)
+            out, lse = E.attn_fwd(q, k, v, causal=causal, softmax_scale=c.softmax_scale, return_lse=True)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            call = E.prepare_bwd(dout, q, k, v, out, lse, dq, dk, dv, causal, c.softmax_scale)
+            t = time_loop([call], K, Wm, torch)
+            fl = W.bwd_flops(2, 2048, 2048, 8, 64, 64, causal)
+            results["bwd_b2h8s2048d64" + ("_causal" if causal else "")] = {
+                "us": t * 1e6, "gflop": fl / 1e9, "tflops": fl / t / 1e12,
+                "pct_mfma_peak": 100 * fl / t / 1e12 / PEAK_TFLOPS}
+            del call, q, k, v, out, lse, dout, dq, dk, dv, c
 
     # ---------------- packed sequences: the headline token budget (2 x 2048) as 7 seeded lengths
     if want("varlen"):

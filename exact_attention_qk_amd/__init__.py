@@ -31,8 +31,9 @@ ATTN_OK = 0
 ERRORS = {-1: "ATTN_E_NULL", -2: "ATTN_E_SHAPE", -3: "ATTN_E_UNSUPPORTED", -4: "ATTN_E_ALIGN",
           -5: "ATTN_E_WORKSPACE", -6: "ATTN_E_OVERFLOW", -7: "ATTN_E_HIP"}
 EXPORTED = ["attn_fwd", "attn_fwd_varlen", "attn_fwd_kvcache", "attn_fwd_kvcache_workspace_size",
-            "rope_apply", "attn_validate_fwd", "attn_validate_varlen", "attn_validate_kvcache",
-            "attn_validate_rope", "attn_last_error", "attn_abi_version"]
+            "attn_bwd", "attn_bwd_workspace_size", "rope_apply", "attn_validate_fwd",
+            "attn_validate_varlen", "attn_validate_kvcache", "attn_validate_bwd", "attn_validate_rope",
+            "attn_last_error", "attn_abi_version"]
 
 
 class AttnError(RuntimeError):
@@ -66,6 +67,17 @@ class VarlenParams(ctypes.Structure):
                 ("window_left", ctypes.c_int), ("window_right", ctypes.c_int)]
 
 
+class BwdParams(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("B", ctypes.c_int), ("Sq", ctypes.c_int),
+                ("Sk", ctypes.c_int), ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int),
+                ("Dqk", ctypes.c_int), ("Dv", ctypes.c_int),
+                ("q", Tensor4), ("k", Tensor4), ("v", Tensor4), ("out", Tensor4), ("dout", Tensor4),
+                ("dq", Tensor4), ("dk", Tensor4), ("dv", Tensor4),
+                ("lse", ctypes.c_void_p), ("causal", ctypes.c_int), ("softmax_scale", ctypes.c_float),
+                ("window_left", ctypes.c_int), ("window_right", ctypes.c_int),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 class KVCacheParams(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int), ("B", ctypes.c_int), ("Sq", ctypes.c_int),
                 ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int), ("Dqk", ctypes.c_int),
@@ -94,6 +106,10 @@ class RopeParams(ctypes.Structure):
 _lib.attn_fwd.argtypes = [ctypes.POINTER(FwdParams), ctypes.c_void_p]
 _lib.attn_fwd_varlen.argtypes = [ctypes.POINTER(VarlenParams), ctypes.c_void_p]
 _lib.attn_validate_varlen.argtypes = [ctypes.POINTER(VarlenParams)]
+_lib.attn_bwd.argtypes = [ctypes.POINTER(BwdParams), ctypes.c_void_p]
+_lib.attn_validate_bwd.argtypes = [ctypes.POINTER(BwdParams)]
+_lib.attn_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdParams)]
+_lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
 _lib.attn_fwd_kvcache.argtypes = [ctypes.POINTER(KVCacheParams), ctypes.c_void_p]
 _lib.attn_fwd_kvcache_workspace_size.argtypes = [ctypes.POINTER(KVCacheParams)]
 _lib.attn_fwd_kvcache_workspace_size.restype = ctypes.c_size_t
@@ -102,8 +118,9 @@ _lib.attn_validate_fwd.argtypes = [ctypes.POINTER(FwdParams)]
 _lib.attn_validate_kvcache.argtypes = [ctypes.POINTER(KVCacheParams)]
 _lib.attn_validate_rope.argtypes = [ctypes.POINTER(RopeParams)]
 _lib.attn_last_error.restype = ctypes.c_char_p
-for _n in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_kvcache", "rope_apply", "attn_validate_fwd",
-           "attn_validate_varlen", "attn_validate_kvcache", "attn_validate_rope", "attn_abi_version"):
+for _n in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_kvcache", "attn_bwd", "rope_apply", "attn_validate_fwd",
+           "attn_validate_varlen", "attn_validate_kvcache", "attn_validate_bwd", "attn_validate_rope",
+           "attn_abi_version"):
     getattr(_lib, _n).restype = ctypes.c_int
 
 _DT = {torch.float16: 0, torch.bfloat16: 1}
@@ -165,6 +182,48 @@ def attn_fwd(q, k, v, causal=False, softmax_scale=None, out=None, return_lse=Fal
     p = fwd_params(q, k, v, out, causal, softmax_scale, lse, window_size)
     _check(_lib.attn_fwd(ctypes.byref(p), _stream(q)))
     return (out, lse) if return_lse else out
+
+
+# ---------------------------------------------------------------- gradients
+
+def bwd_params(q, k, v, out, dout, lse, dq, dk, dv, causal=False, softmax_scale=None,
+               window_size=(-1, -1)):
+    B, Sq, Hq, Dqk = q.shape
+    Sk, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    assert lse.dtype == torch.float32 and lse.is_contiguous() and tuple(lse.shape) == (B, Hq, Sq)
+    return BwdParams(_dtype(q), B, Sq, Sk, Hq, Hkv, Dqk, Dv, _t4(q), _t4(k), _t4(v), _t4(out), _t4(dout),
+                     _t4(dq), _t4(dk), _t4(dv), lse.data_ptr(), int(bool(causal)), _scale(softmax_scale),
+                     int(window_size[0]), int(window_size[1]), None, 0)
+
+
+def _bwd_workspace(p, device):
+    need = int(_lib.attn_bwd_workspace_size(ctypes.byref(p)))
+    ws = torch.empty(need + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    p.workspace = ws.data_ptr() + off if need else None
+    p.workspace_bytes = need
+    return ws
+
+
+def attn_bwd(dout, q, k, v, out, lse, causal=False, softmax_scale=None, window_size=(-1, -1),
+             dq=None, dk=None, dv=None):
+    """Gradients of ``attn_fwd``: returns (dq, dk, dv).  ``out`` and ``lse`` come from the
+    forward call (``return_lse=True``) with the same arguments."""
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=k.dtype, device=k.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=v.dtype, device=v.device) if dv is None else dv
+    p = bwd_params(q, k, v, out, dout, lse, dq, dk, dv, causal, softmax_scale, window_size)
+    ws = _bwd_workspace(p, q.device)
+    _check(_lib.attn_bwd(ctypes.byref(p), _stream(q)))
+    del ws
+    return dq, dk, dv
+
+
+def prepare_bwd(dout, q, k, v, out, lse, dq, dk, dv, causal=False, softmax_scale=None,
+                window_size=(-1, -1)):
+    p = bwd_params(q, k, v, out, dout, lse, dq, dk, dv, causal, softmax_scale, window_size)
+    ws = _bwd_workspace(p, q.device)
+    return PreparedCall(_lib.attn_bwd, p, _stream(q), (dout, q, k, v, out, lse, dq, dk, dv, ws))
 
 
 # ---------------------------------------------------------------- packed sequences
@@ -335,7 +394,8 @@ def prepare_kvcache(q, k_cache, v_cache, k, v, out, *, rotary_cos=None, rotary_s
                          lse, ws))
 
 
-__all__ = ["PreparedCall", "prepare_fwd", "prepare_varlen", "prepare_kvcache", "attn_fwd", "attn_fwd_varlen",
+__all__ = ["PreparedCall", "prepare_fwd", "prepare_varlen", "prepare_kvcache", "prepare_bwd", "attn_bwd",
+           "BwdParams", "bwd_params", "attn_fwd", "attn_fwd_varlen",
            "attn_fwd_kvcache", "rope_apply", "kvcache_workspace_size", "AttnError",
            "FwdParams", "VarlenParams", "KVCacheParams", "RopeParams", "Tensor4", "fwd_params",
            "varlen_params", "kvcache_params",

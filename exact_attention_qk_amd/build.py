@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 
-SOURCES = ["attn_api.hip", "tile_attn.hip", "decode_attn.hip", "rope_append.hip"]
+SOURCES = ["attn_api.hip", "tile_attn.hip", "decode_attn.hip", "rope_append.hip", "attn_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -284,6 +284,55 @@ int validate_varlen(const attn_varlen_params* p) {
   return ok();
 }
 
+int validate_bwd(const attn_bwd_params* p) {
+  if (!p) return fail(ATTN_E_NULL, "params pointer is NULL");
+  int e;
+  if ((e = check_dtype(p->dtype))) return e;
+  if (p->B < 0 || p->Sq < 0 || p->Sk < 0 || p->Hq < 1 || p->Hkv < 1)
+    return fail(ATTN_E_SHAPE, "sizes must satisfy B, Sq, Sk >= 0 and Hq, Hkv >= 1");
+  if (p->Sq >= attn::kNoWindow || p->Sk >= attn::kNoWindow)
+    return fail(ATTN_E_SHAPE, "sequence lengths must be below 2^29");
+  if (p->Hq % p->Hkv)
+    return fail(ATTN_E_SHAPE, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+  const bool dims = (p->Dqk == 64 && p->Dv == 64) || (p->Dqk == 128 && p->Dv == 128) ||
+                    (p->Dqk == 192 && p->Dv == 128);
+  if (!dims)
+    return fail(ATTN_E_UNSUPPORTED, "backward (Dqk, Dv) = (%d, %d) is not one of (64,64), (128,128), (192,128)",
+                p->Dqk, p->Dv);
+  if (p->window_left < -1 || p->window_right < -1)
+    return fail(ATTN_E_SHAPE, "window (%d, %d): each side must be >= -1", p->window_left, p->window_right);
+  if (p->B == 0 || (p->Sq == 0 && p->Sk == 0)) return ok();
+  if (p->Sq > 0) {
+    if ((e = check_tensor(p->q, "q"))) return e;
+    if ((e = check_tensor(p->out, "out"))) return e;
+    if ((e = check_tensor(p->dout, "dout"))) return e;
+    if ((e = check_tensor(p->dq, "dq"))) return e;
+    if (!p->lse) return fail(ATTN_E_NULL, "lse is NULL");
+  }
+  if (p->Sk > 0) {
+    if ((e = check_tensor(p->k, "k"))) return e;
+    if ((e = check_tensor(p->v, "v"))) return e;
+    if ((e = check_tensor(p->dk, "dk"))) return e;
+    if ((e = check_tensor(p->dv, "dv"))) return e;
+  }
+  const size_t need = align_up((size_t)p->B * p->Hq * p->Sq * 2 * sizeof(float));
+  if (p->Sq > 0 && p->Sk > 0) {
+    if (!p->workspace) return fail(ATTN_E_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+    if (p->workspace_bytes < need)
+      return fail(ATTN_E_WORKSPACE, "workspace of %zu bytes required, got %zu", need, p->workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(p->workspace) % kAlign)
+      return fail(ATTN_E_ALIGN, "workspace must be 256-byte aligned");
+  }
+  return ok();
+}
+
+void set_t(const uint16_t*& ptr, int64_t& sb, int64_t& ss, int64_t& sh, const attn_tensor4& t) {
+  ptr = static_cast<const uint16_t*>(t.data); sb = t.stride_b; ss = t.stride_s; sh = t.stride_h;
+}
+void set_t(uint16_t*& ptr, int64_t& sb, int64_t& ss, int64_t& sh, const attn_tensor4& t) {
+  ptr = static_cast<uint16_t*>(t.data); sb = t.stride_b; ss = t.stride_s; sh = t.stride_h;
+}
+
 extern "C" {
 
 int attn_abi_version(void) { return 2; }
@@ -293,6 +342,7 @@ const char* attn_last_error(void) { return g_err.c_str(); }
 int attn_validate_fwd(const attn_fwd_params* p) { return validate_fwd(p); }
 int attn_validate_kvcache(const attn_kvcache_params* p) { return validate_kvcache(p); }
 int attn_validate_varlen(const attn_varlen_params* p) { return validate_varlen(p); }
+int attn_validate_bwd(const attn_bwd_params* p) { return validate_bwd(p); }
 int attn_validate_rope(const attn_rope_params* p) { return validate_rope(p); }
 
 int attn_fwd(const attn_fwd_params* p, void* stream) {
@@ -353,6 +403,54 @@ int attn_fwd_varlen(const attn_varlen_params* p, void* stream) {
   if (p->max_seqlen_q == 0) return ok();
   hipError_t he = attn::run_tile_attn(a, p->dtype == ATTN_DTYPE_BF16, p->Dqk, p->Dv, p->causal != 0, st);
   if (he != hipSuccess) return hip_fail(he, "attn_fwd_varlen launch");
+  return ok();
+}
+
+size_t attn_bwd_workspace_size(const attn_bwd_params* p) {
+  if (!p || p->B < 0 || p->Hq < 1 || p->Sq < 0) return 0;
+  return align_up((size_t)p->B * p->Hq * p->Sq * 2 * sizeof(float));
+}
+
+int attn_bwd(const attn_bwd_params* p, void* stream) {
+  int e = validate_bwd(p);
+  if (e) return e;
+  if (p->B == 0 || (p->Sq == 0 && p->Sk == 0)) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf16 = p->dtype == ATTN_DTYPE_BF16;
+  if (p->Sq == 0 || p->Sk == 0) {
+    // no (query, key) pair: every gradient is zero
+    hipError_t he = hipSuccess;
+    if (p->Sq) he = attn::run_zero_rows(p->dq.data, p->dq.stride_b, p->dq.stride_s, p->dq.stride_h, p->B, p->Sq,
+                                        p->Hq, p->Dqk, st);
+    if (he == hipSuccess && p->Sk)
+      he = attn::run_zero_rows(p->dk.data, p->dk.stride_b, p->dk.stride_s, p->dk.stride_h, p->B, p->Sk, p->Hkv,
+                               p->Dqk, st);
+    if (he == hipSuccess && p->Sk)
+      he = attn::run_zero_rows(p->dv.data, p->dv.stride_b, p->dv.stride_s, p->dv.stride_h, p->B, p->Sk, p->Hkv,
+                               p->Dv, st);
+    if (he != hipSuccess) return hip_fail(he, "attn_bwd zero fill");
+    return ok();
+  }
+  attn::BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  set_t(a.q, a.q_sb, a.q_ss, a.q_sh, p->q);
+  set_t(a.k, a.k_sb, a.k_ss, a.k_sh, p->k);
+  set_t(a.v, a.v_sb, a.v_ss, a.v_sh, p->v);
+  set_t(a.o, a.o_sb, a.o_ss, a.o_sh, p->out);
+  set_t(a.dout, a.do_sb, a.do_ss, a.do_sh, p->dout);
+  set_t(a.dq, a.dq_sb, a.dq_ss, a.dq_sh, p->dq);
+  set_t(a.dk, a.dk_sb, a.dk_ss, a.dk_sh, p->dk);
+  set_t(a.dv, a.dv_sb, a.dv_ss, a.dv_sh, p->dv);
+  a.lse = p->lse;
+  a.ld = static_cast<float*>(p->workspace);
+  a.B = p->B; a.Sq = p->Sq; a.Sk = p->Sk; a.Hq = p->Hq; a.Hkv = p->Hkv; a.group = p->Hq / p->Hkv;
+  a.causal = p->causal ? 1 : 0;
+  a.wl = (p->window_left < 0 || p->window_left > attn::kNoWindow) ? attn::kNoWindow : p->window_left;
+  a.wr = (p->window_right < 0 || p->window_right > attn::kNoWindow) ? attn::kNoWindow : p->window_right;
+  a.c = resolve_c(p->softmax_scale, p->Dqk);
+  a.scale = std::isnan(p->softmax_scale) ? 1.0f / std::sqrt((float)p->Dqk) : p->softmax_scale;
+  hipError_t he = attn::run_attn_bwd(a, bf16, p->Dqk, p->Dv, st);
+  if (he != hipSuccess) return hip_fail(he, "attn_bwd launch");
   return ok();
 }
 

@@ -39,6 +39,26 @@ struct AttnArgs {
   int rd, rinter;             // rotary width (0: none, else a multiple of 16), interleaved pairs
 };
 
+// Gradients of attention (dQ, dK, dV) for a given dO.
+struct BwdArgs {
+  const uint16_t* q;  int64_t q_sb, q_ss, q_sh;
+  const uint16_t* k;  int64_t k_sb, k_ss, k_sh;
+  const uint16_t* v;  int64_t v_sb, v_ss, v_sh;
+  const uint16_t* o;  int64_t o_sb, o_ss, o_sh;
+  const uint16_t* dout; int64_t do_sb, do_ss, do_sh;
+  uint16_t* dq;       int64_t dq_sb, dq_ss, dq_sh;
+  uint16_t* dk;       int64_t dk_sb, dk_ss, dk_sh;
+  uint16_t* dv;       int64_t dv_sb, dv_ss, dv_sh;
+  const float* lse;   // [B, Hq, Sq] from the forward pass (natural log)
+  float* ld;          // workspace [B, Hq, Sq, 2]: lse * log2(e), rowsum(dO * O)
+  int B, Sq, Sk, Hq, Hkv, group;
+  int causal, wl, wr; // masks as in AttnArgs (wl, wr = kNoWindow when unbounded)
+  float c;            // softmax_scale * log2(e)
+  float scale;        // softmax_scale
+  int num_tiles;      // row tiles (dQ kernel) or key tiles (dK/dV kernel) per (batch, head)
+  int xcd_remap;
+};
+
 struct RopeArgs {
   const uint16_t* x;  int64_t x_sb, x_ss, x_sh;
   uint16_t* y;        int64_t y_sb, y_ss, y_sh;

@@ -1,0 +1,477 @@
+// Gradients of exact attention for gfx950: dQ, dK, dV for a given dO, with
+// head_dim_qk != head_dim_v allowed (flash-attention PR #1604 "Support
+// hdimQK != hdimV backward": the backward pass with differing head sizes; the
+// kernels here tile K and V at their own widths, the option that PR names as
+// the better one).
+//
+// With P = exp(scale * Q K^T - lse) recomputed from the forward pass's row
+// log-sum-exp, and D = rowsum(dO * O):
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+//
+// Three launches:
+//  * bwd_prep_kernel: per query row, lse * log2(e) and D into the workspace;
+//  * bwd_dq_kernel: a workgroup owns 128 query rows of one (batch, q head)
+//    (32 per wave, their Q and dO fragments in registers) and streams 32-key
+//    K/V tiles through LDS, like the forward kernel: S^T = K Q^T and
+//    dP^T = V dO^T leave each lane with one query row, so P and dS need no
+//    cross-lane work; dQ^T += K^T dS^T reads K^T with ds_read_b64_tr_b16;
+//  * bwd_dkdv_kernel: the same with the roles of queries and keys swapped: a
+//    workgroup owns 128 keys of one (batch, kv head) (K, V fragments in
+//    registers) and streams 32-row Q / dO / (lse, D) tiles of every q head
+//    that reads this kv head, accumulating dK^T += Q^T dS and dV^T += dO^T P;
+//    summing over the group in registers needs no atomics.
+// Both stream through double-buffered LDS stages filled by buffer loads whose
+// resource ends at the last valid row (rows past it read as zero and are
+// masked).  Masks: key length, causal (bottom-right), local window.
+#include "device_common.hpp"
+#include "attn_args.hpp"
+#include "launchers.hpp"
+
+namespace attn {
+namespace {
+
+__device__ __forceinline__ int perm32(int m) {   // the K-row order of the forward kernel
+  const int a = m >> 3, hh = (m >> 2) & 1, b = m & 3;
+  return 16 * (a >> 1) + 8 * hh + 4 * (a & 1) + b;
+}
+
+template <class T>
+__device__ __forceinline__ uint32_t packw(float a, float b) { return T::pack2(a, b); }
+
+// Row-major tile of 32 rows x D elements in LDS, 16-byte chunks swizzled by
+// row (SK: the K-side swizzle, else the V-side one).
+template <int D, bool SK>
+__device__ __forceinline__ int swz(int r) {
+  return SK ? swz_k<D / 8>(r) : swz_v<D / 8>(r);
+}
+// 16 bytes of row `row`, chunk `chunk` (the A operand of a row-major product)
+template <int D, bool SK>
+__device__ __forceinline__ u32x4 row_frag(const uint16_t* tile, int row, int chunk) {
+  return *reinterpret_cast<const u32x4*>(tile + row * D + ((chunk ^ swz<D, SK>(row)) << 3));
+}
+// transposed operand: elements (rowa..rowa+3, rowa+4..rowa+7) of column col
+template <int D, bool SK>
+__device__ __forceinline__ u32x4 tr_frag(const uint16_t* tile, int rowa, int col) {
+  const int ch = col >> 3, within = col & 7;
+  const u32x2 lo = lds_read_tr16(tile + rowa * D + ((ch ^ swz<D, SK>(rowa)) << 3) + within);
+  const u32x2 hi = lds_read_tr16(tile + (rowa + 4) * D + ((ch ^ swz<D, SK>(rowa + 4)) << 3) + within);
+  return (u32x4){lo[0], lo[1], hi[0], hi[1]};
+}
+// byte offset of this lane's 16-B piece of DMA instruction i of a 32 x D tile
+template <int D, bool SK>
+__device__ __forceinline__ int dma_off(int i, int lane, int64_t row_stride) {
+  constexpr int C = D / 8;
+  const int P = i * 64 + lane, row = P / C, pos = P % C;
+  return (int)(row * row_stride * 2) + ((pos ^ swz<D, SK>(row)) << 4);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- prep
+// one row per (16-byte lanes of dO and O) group; DV / 8 lanes per row
+template <class T, int DV>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  constexpr int LPR = DV / 8, RPW = 64 / LPR;
+  const int lane = threadIdx.x & 63, sub = lane / LPR, c = lane - sub * LPR;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + sub;
+  const int64_t total = (int64_t)a.B * a.Hq * a.Sq;
+  const bool ok = sub < RPW && row < total;
+  const int64_t rr = ok ? row : 0;
+  const int i = (int)(rr % a.Sq);
+  const int64_t bh = rr / a.Sq;
+  const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+  const u32x4 dv = ldg16(a.dout + (int64_t)b * a.do_sb + (int64_t)i * a.do_ss + (int64_t)h * a.do_sh + 8 * c);
+  const u32x4 ov = ldg16(a.o + (int64_t)b * a.o_sb + (int64_t)i * a.o_ss + (int64_t)h * a.o_sh + 8 * c);
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc += T::to_f32((uint16_t)(dv[e] & 0xFFFFu)) * T::to_f32((uint16_t)(ov[e] & 0xFFFFu));
+    acc += T::to_f32((uint16_t)(dv[e] >> 16)) * T::to_f32((uint16_t)(ov[e] >> 16));
+  }
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m);
+  if (ok && c == 0) {
+    const float l = a.lse[rr];
+    a.ld[2 * rr + 0] = l * 1.4426950408889634f;
+    a.ld[2 * rr + 1] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+template <class T, int DQK, int DV, bool CAUSAL, bool WIN>
+__global__ __launch_bounds__(256, (DQK > 128 ? 1 : 2)) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int KS = DQK / 16, VS = DV / 16, QB = DQK / 32;
+  constexpr int KT = 32 * DQK, VT = 32 * DV, STAGE = KT + VT;
+  constexpr int NIK = 32 * DQK / 8 / 64, NIV = 32 * DV / 8 / 64;   // DMA instructions per tile
+  constexpr int JK = (NIK + 3) / 4, JV = (NIV + 3) / 4;
+  constexpr int OSTR = DQK + 8;
+  constexpr int LDS_BYTES = (2 * STAGE * 2 > 128 * OSTR * 2) ? 2 * STAGE * 2 : 128 * OSTR * 2;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
+  uint16_t* lds16 = reinterpret_cast<uint16_t*>(smem);
+  const uint32_t smem_addr = (uint32_t)reinterpret_cast<uintptr_t>((LDS_AS void*)smem);
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hh = lane >> 5;
+  int u = blockIdx.x;
+  if (a.xcd_remap) {
+    const int per = gridDim.x >> 3;
+    u = (u & 7) * per + (u >> 3);
+  }
+  const int bh = u / a.num_tiles, qt = u - bh * a.num_tiles;
+  const int b = bh / a.Hq, hq = bh - b * a.Hq, hkv = hq / a.group;
+  const int L = a.Sk, off = a.Sk - a.Sq;
+  const int wrgt = WIN ? (CAUSAL ? min(a.wr, 0) : a.wr) : 0;
+  const int wlft = WIN ? a.wl : 0;
+  const int q0 = qt * 128;
+  const int rows_end = min(q0 + 128, a.Sq);
+  int kend = L, kbeg = 0;
+  if (WIN || CAUSAL) kend = max(0, min(L, off + rows_end + wrgt));
+  if (WIN) kbeg = min(kend, max(0, off + q0 - wlft));
+  const int t_lo = kbeg / 32;
+  const int ntiles = max(0, (kend + 31) / 32 - t_lo);
+
+  const int row = q0 + w * 32 + (lane & 31);      // this lane's query row
+  const bool row_ok = row < a.Sq;
+  const int rc = min(row, a.Sq - 1);
+  const int qpos = off + row;
+  const uint16_t* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
+  const uint16_t* vbase = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+
+  u32x4 qf[KS], dof[VS];
+  {
+    const uint16_t* qr = a.q + (int64_t)b * a.q_sb + (int64_t)rc * a.q_ss + (int64_t)hq * a.q_sh;
+    const uint16_t* dr = a.dout + (int64_t)b * a.do_sb + (int64_t)rc * a.do_ss + (int64_t)hq * a.do_sh;
+#pragma unroll
+    for (int st = 0; st < KS; ++st) qf[st] = ldg16(qr + 16 * st + 8 * hh);
+#pragma unroll
+    for (int st = 0; st < VS; ++st) dof[st] = ldg16(dr + 16 * st + 8 * hh);
+  }
+  const int64_t lrow = ((int64_t)b * a.Hq + hq) * a.Sq + rc;
+  const float lse2 = a.ld[2 * lrow], Drow = a.ld[2 * lrow + 1];
+
+  int koff[JK], voff[JV];
+#pragma unroll
+  for (int j = 0; j < JK; ++j) koff[j] = dma_off<DQK, true>(min(w + 4 * j, NIK - 1), lane, a.k_ss);
+#pragma unroll
+  for (int j = 0; j < JV; ++j) voff[j] = dma_off<DV, false>(min(w + 4 * j, NIV - 1), lane, a.v_ss);
+  auto issue = [&](int t, int s) {
+    const int key0 = t * 32, rows = min(32, L - key0);
+    const i32x4 rk = make_rsrc(kbase + (int64_t)key0 * a.k_ss, rows * (int)a.k_ss * 2);
+    const i32x4 rv = make_rsrc(vbase + (int64_t)key0 * a.v_ss, rows * (int)a.v_ss * 2);
+    const uint32_t kd = smem_addr + (uint32_t)(s * STAGE) * 2, vd = kd + KT * 2;
+#pragma unroll
+    for (int j = 0; j < JK; ++j)
+      if (w + 4 * j < NIK) dma_b128(rk, kd + (w + 4 * j) * 1024, koff[j]);
+#pragma unroll
+    for (int j = 0; j < JV; ++j)
+      if (w + 4 * j < NIV) dma_b128(rv, vd + (w + 4 * j) * 1024, voff[j]);
+  };
+
+  f32x16 dq[QB];
+#pragma unroll
+  for (int i = 0; i < QB; ++i) dq[i] = (f32x16){};
+  const int grp = lane >> 4, tr_t = (lane & 15) >> 2, tr_q = lane & 3;
+  const float c = a.c;
+
+  if (ntiles > 0) issue(t_lo, 0);
+  for (int it = 0; it < ntiles; ++it) {
+    const int s = it & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this lane's part of tile it landed
+    __syncthreads();                      // ... every lane's; stage s^1 is free again
+    if (it + 1 < ntiles) issue(t_lo + it + 1, s ^ 1);
+    const int key0 = (t_lo + it) * 32;
+    const uint16_t* kt = lds16 + s * STAGE;
+    const uint16_t* vt = kt + KT;
+    // S^T = K Q^T and dP^T = V dO^T, keys in the forward kernel's order
+    const int prow = perm32(lane & 31);
+    f32x16 sc = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+    for (int st = 0; st < KS; ++st) sc = T::mfma32(row_frag<DQK, true>(kt, prow, 2 * st + hh), qf[st], sc);
+#pragma unroll
+    for (int st = 0; st < VS; ++st) dp = T::mfma32(row_frag<DV, false>(vt, prow, 2 * st + hh), dof[st], dp);
+    u32x4 dsf[2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      float d[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * t2 + e;
+        const int key = key0 + 16 * t2 + 8 * hh + e;
+        bool ok = row_ok && key < L;
+        if (WIN || CAUSAL) ok = ok && key <= qpos + wrgt;
+        if (WIN) ok = ok && key >= qpos - wlft;
+        const float p = ok ? fast_exp2(__builtin_fmaf(sc[r], c, -lse2)) : 0.f;
+        d[e] = p * (dp[r] - Drow);
+      }
+      dsf[t2] = (u32x4){packw<T>(d[0], d[1]), packw<T>(d[2], d[3]), packw<T>(d[4], d[5]), packw<T>(d[6], d[7])};
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int rowa = 16 * t2 + 8 * hh + tr_t;
+#pragma unroll
+      for (int i = 0; i < QB; ++i)
+        dq[i] = T::mfma32(tr_frag<DQK, true>(kt, rowa, i * 32 + 16 * (grp & 1) + 4 * tr_q), dsf[t2], dq[i]);
+    }
+  }
+
+  // epilogue: scale, round, stage through LDS, 16-byte stores of whole rows
+  __syncthreads();
+  uint16_t* st_o = lds16 + w * 32 * OSTR;
+#pragma unroll
+  for (int i = 0; i < QB; ++i)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int d = i * 32 + 8 * a4 + 4 * hh;
+      *reinterpret_cast<u32x2*>(st_o + (lane & 31) * OSTR + d) =
+          (u32x2){T::pack2(dq[i][4 * a4 + 0] * a.scale, dq[i][4 * a4 + 1] * a.scale),
+                  T::pack2(dq[i][4 * a4 + 2] * a.scale, dq[i][4 * a4 + 3] * a.scale)};
+    }
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  constexpr int CH = DQK / 8;
+  for (int id = lane; id < 32 * CH; id += 64) {
+    const int r = id / CH, ch = id - r * CH;
+    const int qrow = q0 + w * 32 + r;
+    if (qrow < a.Sq)
+      stg16(a.dq + (int64_t)b * a.dq_sb + (int64_t)qrow * a.dq_ss + (int64_t)hq * a.dq_sh + ch * 8,
+            *reinterpret_cast<const u32x4*>(st_o + r * OSTR + ch * 8));
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+template <class T, int DQK, int DV, bool CAUSAL, bool WIN>
+__global__ __launch_bounds__(256, (DQK > 64 ? 1 : 2)) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int KS = DQK / 16, VS = DV / 16, KB = DQK / 32, VB = DV / 32;
+  constexpr int QT = 32 * DQK, OT = 32 * DV, LT = 32 * 2 * 2;     // elements: Q, dO, (lse, D) tiles
+  constexpr int STAGE = QT + OT + LT;
+  constexpr int NIQ = 32 * DQK / 8 / 64, NIO = 32 * DV / 8 / 64;
+  constexpr int JQ = (NIQ + 3) / 4, JO = (NIO + 3) / 4;
+  constexpr int OSTR = (DQK > DV ? DQK : DV) + 8;
+  constexpr int LDS_BYTES = (2 * STAGE * 2 > 128 * OSTR * 2) ? 2 * STAGE * 2 : 128 * OSTR * 2;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
+  uint16_t* lds16 = reinterpret_cast<uint16_t*>(smem);
+  const uint32_t smem_addr = (uint32_t)reinterpret_cast<uintptr_t>((LDS_AS void*)smem);
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hh = lane >> 5;
+  int u = blockIdx.x;
+  if (a.xcd_remap) {
+    const int per = gridDim.x >> 3;
+    u = (u & 7) * per + (u >> 3);
+  }
+  const int bh = u / a.num_tiles, kt_i = u - bh * a.num_tiles;
+  const int b = bh / a.Hkv, hkv = bh - b * a.Hkv;
+  const int L = a.Sk, off = a.Sk - a.Sq;
+  const int wrgt = WIN ? (CAUSAL ? min(a.wr, 0) : a.wr) : 0;
+  const int wlft = WIN ? a.wl : 0;
+  const int k0 = kt_i * 128;
+  const int k1 = min(k0 + 128, L);
+  // query rows that see any key of [k0, k1): position p with k0 - wrgt <= p <= k1 - 1 + wlft
+  int r_lo = 0, r_hi = a.Sq;
+  if (WIN || CAUSAL) r_lo = min(a.Sq, max(0, k0 - wrgt - off));
+  if (WIN) r_hi = max(r_lo, min(a.Sq, k1 - 1 + wlft - off + 1));
+  const int rb_lo = r_lo / 32;
+  const int nrb = max(0, (r_hi + 31) / 32 - rb_lo);   // row blocks per q head
+  const int nsteps = nrb * a.group;
+
+  const int key = k0 + w * 32 + (lane & 31);          // this lane's key
+  const bool key_ok = key < L;
+  const int kc = min(key, L - 1);
+  u32x4 kf[KS], vf[VS];
+  {
+    const uint16_t* kr = a.k + (int64_t)b * a.k_sb + (int64_t)kc * a.k_ss + (int64_t)hkv * a.k_sh;
+    const uint16_t* vr = a.v + (int64_t)b * a.v_sb + (int64_t)kc * a.v_ss + (int64_t)hkv * a.v_sh;
+#pragma unroll
+    for (int st = 0; st < KS; ++st) kf[st] = ldg16(kr + 16 * st + 8 * hh);
+#pragma unroll
+    for (int st = 0; st < VS; ++st) vf[st] = ldg16(vr + 16 * st + 8 * hh);
+  }
+
+  int qoff[JQ], ooff[JO];
+#pragma unroll
+  for (int j = 0; j < JQ; ++j) qoff[j] = dma_off<DQK, true>(min(w + 4 * j, NIQ - 1), lane, a.q_ss);
+#pragma unroll
+  for (int j = 0; j < JO; ++j) ooff[j] = dma_off<DV, false>(min(w + 4 * j, NIO - 1), lane, a.do_ss);
+  // step n: q head hkv * group + n / nrb, row block rb_lo + n % nrb
+  auto issue = [&](int n, int s) {
+    const int h = hkv * a.group + n / nrb;
+    const int r0 = (rb_lo + n % nrb) * 32, rows = min(32, a.Sq - r0);
+    const i32x4 rq = make_rsrc(a.q + (int64_t)b * a.q_sb + (int64_t)r0 * a.q_ss + (int64_t)h * a.q_sh,
+                               rows * (int)a.q_ss * 2);
+    const i32x4 ro = make_rsrc(a.dout + (int64_t)b * a.do_sb + (int64_t)r0 * a.do_ss + (int64_t)h * a.do_sh,
+                               rows * (int)a.do_ss * 2);
+    const uint32_t qd = smem_addr + (uint32_t)(s * STAGE) * 2, od = qd + QT * 2, ldd = od + OT * 2;
+#pragma unroll
+    for (int j = 0; j < JQ; ++j)
+      if (w + 4 * j < NIQ) dma_b128(rq, qd + (w + 4 * j) * 1024, qoff[j]);
+#pragma unroll
+    for (int j = 0; j < JO; ++j)
+      if (w + 4 * j < NIO) dma_b128(ro, od + (w + 4 * j) * 1024, ooff[j]);
+    if (w == 0 && lane < 16) {   // 32 rows of (lse2, D): 256 bytes
+      const i32x4 rl = make_rsrc(a.ld + 2 * (((int64_t)b * a.Hq + h) * a.Sq + r0), rows * 8);
+      dma_b128(rl, ldd, lane * 16);
+    }
+  };
+
+  f32x16 dk[KB], dv[VB];
+#pragma unroll
+  for (int i = 0; i < KB; ++i) dk[i] = (f32x16){};
+#pragma unroll
+  for (int i = 0; i < VB; ++i) dv[i] = (f32x16){};
+  const int grp = lane >> 4, tr_t = (lane & 15) >> 2, tr_q = lane & 3;
+  const float c = a.c;
+
+  if (nsteps > 0) issue(0, 0);
+  for (int n = 0; n < nsteps; ++n) {
+    const int s = n & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (n + 1 < nsteps) issue(n + 1, s ^ 1);
+    const int r0 = (rb_lo + n % nrb) * 32;
+    const uint16_t* qt = lds16 + s * STAGE;
+    const uint16_t* ot = qt + QT;
+    const float* lt = reinterpret_cast<const float*>(ot + OT);
+    // S = Q K^T and dP = dO V^T: a lane owns a key; its registers cover rows
+    // r0 + 16 (r >> 3) + 8 hh + (r & 7)
+    const int prow = perm32(lane & 31);
+    f32x16 sc = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+    for (int st = 0; st < KS; ++st) sc = T::mfma32(row_frag<DQK, true>(qt, prow, 2 * st + hh), kf[st], sc);
+#pragma unroll
+    for (int st = 0; st < VS; ++st) dp = T::mfma32(row_frag<DV, false>(ot, prow, 2 * st + hh), vf[st], dp);
+    u32x4 pf[2], dsf[2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const f32x4 l0 = *reinterpret_cast<const f32x4*>(lt + 2 * (16 * t2 + 8 * hh));
+      const f32x4 l1 = *reinterpret_cast<const f32x4*>(lt + 2 * (16 * t2 + 8 * hh) + 4);
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(lt + 2 * (16 * t2 + 8 * hh) + 8);
+      const f32x4 l3 = *reinterpret_cast<const f32x4*>(lt + 2 * (16 * t2 + 8 * hh) + 12);
+      const float lsev[8] = {l0[0], l0[2], l1[0], l1[2], l2[0], l2[2], l3[0], l3[2]};
+      const float dv8[8] = {l0[1], l0[3], l1[1], l1[3], l2[1], l2[3], l3[1], l3[3]};
+      float p[8], d[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * t2 + e;
+        const int qrow = r0 + 16 * t2 + 8 * hh + e;
+        const int qpos = off + qrow;
+        bool ok = key_ok && qrow < a.Sq;
+        if (WIN || CAUSAL) ok = ok && key <= qpos + wrgt;
+        if (WIN) ok = ok && key >= qpos - wlft;
+        p[e] = ok ? fast_exp2(__builtin_fmaf(sc[r], c, -lsev[e])) : 0.f;
+        d[e] = p[e] * (dp[r] - dv8[e]);
+      }
+      pf[t2] = (u32x4){packw<T>(p[0], p[1]), packw<T>(p[2], p[3]), packw<T>(p[4], p[5]), packw<T>(p[6], p[7])};
+      dsf[t2] = (u32x4){packw<T>(d[0], d[1]), packw<T>(d[2], d[3]), packw<T>(d[4], d[5]), packw<T>(d[6], d[7])};
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int rowa = 16 * t2 + 8 * hh + tr_t;
+#pragma unroll
+      for (int i = 0; i < VB; ++i)
+        dv[i] = T::mfma32(tr_frag<DV, false>(ot, rowa, i * 32 + 16 * (grp & 1) + 4 * tr_q), pf[t2], dv[i]);
+#pragma unroll
+      for (int i = 0; i < KB; ++i)
+        dk[i] = T::mfma32(tr_frag<DQK, true>(qt, rowa, i * 32 + 16 * (grp & 1) + 4 * tr_q), dsf[t2], dk[i]);
+    }
+  }
+
+  // epilogue: dK = scale dK^T^T, dV = dV^T^T, staged through LDS per wave
+  __syncthreads();
+  uint16_t* st_o = lds16 + w * 32 * OSTR;
+  auto store = [&](const f32x16* acc, int NB, int D, float mul, uint16_t* gbase, int64_t g_ss) {
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d = i * 32 + 8 * a4 + 4 * hh;
+        *reinterpret_cast<u32x2*>(st_o + (lane & 31) * OSTR + d) =
+            (u32x2){T::pack2(acc[i][4 * a4 + 0] * mul, acc[i][4 * a4 + 1] * mul),
+                    T::pack2(acc[i][4 * a4 + 2] * mul, acc[i][4 * a4 + 3] * mul)};
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+    const int CH = D / 8;
+    for (int id = lane; id < 32 * CH; id += 64) {
+      const int r = id / CH, ch = id - r * CH;
+      const int kk = k0 + w * 32 + r;
+      if (kk < L) stg16(gbase + (int64_t)kk * g_ss + ch * 8, *reinterpret_cast<const u32x4*>(st_o + r * OSTR + ch * 8));
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+  };
+  store(dk, KB, DQK, a.scale, a.dk + (int64_t)b * a.dk_sb + (int64_t)hkv * a.dk_sh, a.dk_ss);
+  store(dv, VB, DV, 1.f, a.dv + (int64_t)b * a.dv_sb + (int64_t)hkv * a.dv_sh, a.dv_ss);
+}
+
+// ---------------------------------------------------------------- launchers
+template <class T, int DQK, int DV, bool CAUSAL, bool WIN>
+static hipError_t launch_bwd(const BwdArgs& a0, hipStream_t st) {
+  BwdArgs a = a0;
+  {
+    const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
+    const int rpb = 4 * (64 / (DV / 8));
+    hipLaunchKernelGGL((bwd_prep_kernel<T, DV>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    a.num_tiles = (a.Sq + 127) / 128;
+    const int64_t units = (int64_t)a.B * a.Hq * a.num_tiles;
+    a.xcd_remap = units % 8 == 0;
+    hipLaunchKernelGGL((bwd_dq_kernel<T, DQK, DV, CAUSAL, WIN>), dim3((unsigned)units), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  a.num_tiles = (a.Sk + 127) / 128;
+  const int64_t units = (int64_t)a.B * a.Hkv * a.num_tiles;
+  a.xcd_remap = units % 8 == 0;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, DQK, DV, CAUSAL, WIN>), dim3((unsigned)units), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <class T, int DQK, int DV>
+static hipError_t launch_bwd_c(const BwdArgs& a, hipStream_t st) {
+  const bool win = a.wl < kNoWindow || a.wr < kNoWindow;
+  if (win) return a.causal ? launch_bwd<T, DQK, DV, true, true>(a, st) : launch_bwd<T, DQK, DV, false, true>(a, st);
+  return a.causal ? launch_bwd<T, DQK, DV, true, false>(a, st) : launch_bwd<T, DQK, DV, false, false>(a, st);
+}
+
+template <class T>
+static hipError_t launch_bwd_t(const BwdArgs& a, int dqk, int dv, hipStream_t st) {
+  if (dqk == 64 && dv == 64) return launch_bwd_c<T, 64, 64>(a, st);
+  if (dqk == 128 && dv == 128) return launch_bwd_c<T, 128, 128>(a, st);
+  if (dqk == 192 && dv == 128) return launch_bwd_c<T, 192, 128>(a, st);
+  return hipErrorInvalidValue;
+}
+
+// zero a [B, S, H, D] 16-bit tensor with element strides (16 bytes per thread)
+__global__ __launch_bounds__(256) void zero_rows_kernel(uint16_t* p, int64_t sb, int64_t ss, int64_t sh, int B,
+                                                        int S, int H, int D) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int CH = D / 8;
+  const int64_t total = (int64_t)B * S * H * CH;
+  if (i >= total) return;
+  const int ch = (int)(i % CH);
+  const int64_t r = i / CH;
+  const int h = (int)(r % H), s = (int)((r / H) % S), b = (int)(r / ((int64_t)H * S));
+  stg16(p + (int64_t)b * sb + (int64_t)s * ss + (int64_t)h * sh + ch * 8, (u32x4){0u, 0u, 0u, 0u});
+}
+
+hipError_t run_zero_rows(void* data, int64_t sb, int64_t ss, int64_t sh, int B, int S, int H, int D,
+                         hipStream_t st) {
+  const int64_t total = (int64_t)B * S * H * (D / 8);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                     static_cast<uint16_t*>(data), sb, ss, sh, B, S, H, D);
+  return hipGetLastError();
+}
+
+hipError_t run_attn_bwd(const BwdArgs& a, int dtype_bf16, int dqk, int dv, hipStream_t st) {
+  if (a.B == 0 || a.Hq == 0) return hipSuccess;
+  return dtype_bf16 ? launch_bwd_t<BF16>(a, dqk, dv, st) : launch_bwd_t<F16>(a, dqk, dv, st);
+}
+
+}  // namespace attn

@@ -9,4 +9,7 @@ hipError_t run_tile_attn(const AttnArgs& a, int dtype_bf16, int dqk, int dv, boo
 hipError_t run_decode_attn(const AttnArgs& a, int dtype_bf16, int dqk, int dv, bool causal,
                            hipStream_t st);
 hipError_t run_rope_rows(const RowSet* sets, int nsets, int dtype_bf16, hipStream_t st);
+hipError_t run_attn_bwd(const BwdArgs& a, int dtype_bf16, int dqk, int dv, hipStream_t st);
+hipError_t run_zero_rows(void* data, int64_t sb, int64_t ss, int64_t sh, int B, int S, int H, int D,
+                         hipStream_t st);
 }  // namespace attn

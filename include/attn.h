@@ -209,6 +209,37 @@ typedef struct attn_kvcache_params {
 size_t attn_fwd_kvcache_workspace_size(const attn_kvcache_params* p);
 int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream);
 
+/* ----------------------------------------------------------------- attn_bwd
+ * Gradients of attn_fwd (flash-attention PR #1604 "Support hdimQK != hdimV
+ * backward": dQ, dK, dV with head_dim_qk != head_dim_v).  For the forward
+ * call with the same q, k, v, causal, softmax_scale and window, and an
+ * upstream gradient dout of the output:
+ *   P = softmax(scale * q k^T + mask), dv = P^T dout, dP = dout v^T,
+ *   dS = P * (dP - rowsum(dout * out)), dq = scale * dS k, dk = scale * dS^T q,
+ * with dk, dv of a kv head summed over the q heads that read it.
+ * q, k, v, out, dout: as in attn_fwd (out is the forward output); read.
+ * lse [B, Hq, Sq] fp32 contiguous: the forward's lse; read.
+ * dq [B, Sq, Hq, Dqk], dk [B, Sk, Hkv, Dqk], dv [B, Sk, Hkv, Dv]: written
+ *     (every element, zeros where no query reaches a key).
+ * (Dqk, Dv) in {(64, 64), (128, 128), (192, 128)}; other supported forward
+ * sizes return ATTN_E_UNSUPPORTED here.
+ * workspace: attn_bwd_workspace_size(p) bytes, 256-byte aligned, scratch.
+ */
+typedef struct attn_bwd_params {
+  attn_dtype dtype;
+  int B, Sq, Sk, Hq, Hkv, Dqk, Dv;
+  attn_tensor4 q, k, v, out, dout, dq, dk, dv;
+  const float* lse;
+  int causal;
+  float softmax_scale;
+  int window_left, window_right;
+  void* workspace;
+  size_t workspace_bytes;
+} attn_bwd_params;
+
+size_t attn_bwd_workspace_size(const attn_bwd_params* p);
+int attn_bwd(const attn_bwd_params* p, void* stream);
+
 /* -------------------------------------------------------------- rope_apply
  * x   [B, S, H, D]  read
  * out [B, S, H, D]  written; may be the same memory as x (in place)
@@ -238,6 +269,7 @@ int rope_apply(const attn_rope_params* p, void* stream);
 int attn_validate_fwd(const attn_fwd_params* p);
 int attn_validate_kvcache(const attn_kvcache_params* p);
 int attn_validate_varlen(const attn_varlen_params* p);
+int attn_validate_bwd(const attn_bwd_params* p);
 int attn_validate_rope(const attn_rope_params* p);
 const char* attn_last_error(void);
 int attn_abi_version(void);  /* 2 */

@@ -109,6 +109,25 @@ def test_validate_varlen():
     assert E.lib().attn_validate_varlen(ctypes.byref(p)) == -3
 
 
+def test_validate_bwd():
+    q = _t((2, 8, 4, 64))
+    k = _t((2, 8, 2, 64))
+    lse = torch.zeros(2, 4, 8)
+    p = E.bwd_params(q, k, k, q, q, lse, q, k, k)
+    assert E.lib().attn_validate_bwd(ctypes.byref(p)) == -5          # workspace missing
+    need = E.lib().attn_bwd_workspace_size(ctypes.byref(p))
+    assert need == ((2 * 4 * 8 * 8 + 255) // 256) * 256
+    ws = torch.zeros(need + 512, dtype=torch.uint8)
+    p.workspace, p.workspace_bytes = ws.data_ptr() + (-ws.data_ptr()) % 256, need
+    assert E.lib().attn_validate_bwd(ctypes.byref(p)) == 0
+    p.Dqk = p.Dv = 16
+    assert E.lib().attn_validate_bwd(ctypes.byref(p)) == -3         # no backward at head size 16
+    p = E.bwd_params(q, k, k, q, q, lse, q, k, k)
+    p.workspace, p.workspace_bytes = ws.data_ptr() + (-ws.data_ptr()) % 256, need
+    p.lse = None
+    assert E.lib().attn_validate_bwd(ctypes.byref(p)) == -1
+
+
 def test_binding_rejects_other_dtypes_before_any_launch():
     q = torch.zeros(1, 4, 1, 64)
     with pytest.raises(AttnError):

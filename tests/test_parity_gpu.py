@@ -12,7 +12,8 @@ import pytest
 import torch
 
 import workloads as W
-from oracle import attention_ref, attention_varlen_ref, dtype_bits, kvcache_ref, rope_ref, to_f64
+from oracle import (attention_bwd_ref, attention_ref, attention_varlen_ref, dtype_bits, kvcache_ref,
+                    rope_ref, to_f64)
 
 pytestmark = pytest.mark.gpu
 TOL = {"fp16": 2e-3, "bf16": 1.5e-2}
@@ -439,6 +440,67 @@ def test_varlen_equal_lengths_bitwise_batched():
     ob = E().attn_fwd(q, k, v, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(ob.view(B * S, 4, 64), out)
+
+
+# ---------------------------------------------------------------- gradients
+# dq, dk, dv are sums over rows or keys, so their bar scales with their size:
+# max-abs error <= TOL[dtype] * max(1, max |reference|)
+
+def _bwd_check(case, window=(-1, -1), seed=0):
+    q, k, v = dev(case.q), dev(case.k), dev(case.v)
+    g = torch.Generator().manual_seed(seed + 1000)
+    dout_c = torch.randn(q.shape[:3] + (v.shape[3],), generator=g).to(q.dtype)
+    dout = dev(dout_c)
+    out, lse = E().attn_fwd(q, k, v, causal=case.causal, softmax_scale=case.softmax_scale, return_lse=True,
+                            window_size=window)
+    dq, dk, dv = E().attn_bwd(dout, q, k, v, out, lse, causal=case.causal,
+                              softmax_scale=case.softmax_scale, window_size=window)
+    torch.cuda.synchronize()
+    rq, rk, rv = attention_bwd_ref(to_f64(case.q), to_f64(case.k), to_f64(case.v), to_f64(dout_c),
+                                   causal=case.causal, softmax_scale=case.softmax_scale, window=window)
+    errs = []
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        err = maxabs(got, ref)
+        bar = TOL[case.dtype] * max(1.0, float(np.max(np.abs(ref))))
+        assert err <= bar, "%s max abs err %.3e > %.3e" % (name, err, bar)
+        errs.append(err)
+    return errs
+
+
+@pytest.mark.parametrize("dqk,dv,dtype", [(64, 64, "fp16"), (128, 128, "bf16"), (192, 128, "bf16"),
+                                          (64, 64, "bf16"), (128, 128, "fp16")])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_multi_tile_ragged(dqk, dv, dtype, causal):
+    # 200 rows/keys: two 128-row tiles each way plus ragged tails; GQA 4:2
+    case = W.random_fwd(2, 200, 200, 4, 2, dqk, dv, dtype, causal, seed=dqk + 5 * causal)
+    _bwd_check(case, seed=dqk)
+
+
+@pytest.mark.parametrize("sq,sk", [(100, 333), (333, 100), (1, 70), (70, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_sq_ne_sk(sq, sk, causal):
+    case = W.random_fwd(1, sq, sk, 2, 1, 64, 64, "fp16", causal, seed=sq + sk)
+    _bwd_check(case, seed=sq)
+
+
+@pytest.mark.parametrize("window", [(0, 0), (37, 5), (-1, 20), (100, -1)])
+def test_bwd_window(window):
+    case = W.random_fwd(1, 300, 300, 4, 2, 128, 128, "bf16", True, seed=3 + window[0])
+    _bwd_check(case, window=window, seed=7)
+
+
+def test_bwd_gqa_group_of_eight():
+    case = W.random_fwd(1, 150, 150, 8, 1, 64, 64, "fp16", True, seed=9)
+    _bwd_check(case, seed=9)
+
+
+def test_bwd_no_keys_gives_zero_gradients():
+    q = torch.randn(1, 5, 2, 64, device=DEV).half()
+    k = torch.zeros(1, 0, 2, 64, device=DEV).half()
+    out, lse = E().attn_fwd(q, k, k, return_lse=True)
+    dq, dk, dv = E().attn_bwd(torch.randn_like(q), q, k, k, out, lse)
+    torch.cuda.synchronize()
+    assert (dq.float() == 0).all()
 
 
 # ---------------------------------------------------------------- rope_apply

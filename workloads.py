@@ -272,6 +272,13 @@ def fwd_flops(B, Sq, Sk, Hq, Dqk, Dv, causal, window=(-1, -1)):
     return 2.0 * (Dqk + Dv) * B * Hq * pairs
 
 
+def bwd_flops(B, Sq, Sk, Hq, Dqk, Dv, causal, window=(-1, -1)):
+    """Gradient work: five products per unmasked (query, key) pair -- S = Q K^T, dV += P^T dO,
+    dP = dO V^T, dQ += dS K, dK += dS^T Q -- i.e. 2*(3*Dqk + 2*Dv) flop per pair."""
+    pairs = fwd_flops(B, Sq, Sk, Hq, 1, 0, causal, window) / 2.0
+    return 2.0 * (3 * Dqk + 2 * Dv) * pairs
+
+
 def kvcache_pairs(lens, Sq, snew, causal):
     tot = 0
     for c in lens:
