@@ -307,7 +307,10 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void bwd_dq_kernel(BwdArgs a) {
 // The same split with the roles of queries and keys swapped: a wave owns 32
 // keys, the NS groups walk disjoint (q head, 32-row block) steps, and their
 // dK/dV partial sums are added through LDS.  PAIR (causal): key tiles (p, n-1-p).
-template <class T, int DQK, int DV, bool CAUSAL, bool WIN, int NR, int NS, bool PAIR, int MINW>
+// KVL: K and V stay in LDS (a 32-key tile per wave column, shared by the
+// groups) instead of registers, which leaves room for two waves per SIMD at
+// the larger head sizes.
+template <class T, int DQK, int DV, bool CAUSAL, bool WIN, int NR, int NS, bool PAIR, int MINW, bool KVL>
 __global__ __launch_bounds__(64 * NR * NS, MINW) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int KS = DQK / 16, VS = DV / 16, KB = DQK / 32, VB = DV / 32;
   constexpr int BK = 32 * NR;
@@ -316,7 +319,8 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void bwd_dkdv_kernel(BwdArgs a)
   constexpr int NIQ = DQK / 16, NIO = DV / 16;
   constexpr int JQ = (NIQ + NR - 1) / NR, JO = (NIO + NR - 1) / NR;
   constexpr int OSTR = (DQK > DV ? DQK : DV) + 8;
-  constexpr int LDS_KV = NS * 2 * STAGE * 2;
+  constexpr int RES = KVL ? NR * 32 * (DQK + DV) : 0;            // elements of resident K/V tiles
+  constexpr int LDS_KV = RES * 2 + NS * 2 * STAGE * 2;
   constexpr int MERGE = (NS - 1) * NR * (KB + VB) * 16 * 64 * 4;
   constexpr int LDS_O = BK * OSTR * 2;
   constexpr int LDS_A = LDS_KV > MERGE ? LDS_KV : MERGE;
@@ -377,8 +381,22 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void bwd_dkdv_kernel(BwdArgs a)
     const int key = wk0 + (lane & 31);                  // this lane's key
     const bool key_ok = key < L;
     const int kc = min(key, L - 1);
-    u32x4 kf[KS], vf[VS];
-    {
+    u32x4 kf[KVL ? 1 : KS], vf[KVL ? 1 : VS];
+    const uint16_t* kres = lds16 + rw * 32 * (DQK + DV);
+    const uint16_t* vres = kres + 32 * DQK;
+    if constexpr (KVL) {
+      // this wave column's K and V tiles; the NS waves that share it split the copies
+      if (wk0 < L) {
+        const int rows = min(32, L - wk0);
+        const i32x4 rk = make_rsrc(a.k + (int64_t)b * a.k_sb + (int64_t)wk0 * a.k_ss + (int64_t)hkv * a.k_sh,
+                                   rows * (int)a.k_ss * 2);
+        const i32x4 rv = make_rsrc(a.v + (int64_t)b * a.v_sb + (int64_t)wk0 * a.v_ss + (int64_t)hkv * a.v_sh,
+                                   rows * (int)a.v_ss * 2);
+        const uint32_t kd = smem_addr + (uint32_t)(rw * 32 * (DQK + DV)) * 2, vd = kd + 32 * DQK * 2;
+        for (int i = g; i < NIQ; i += NS) dma_b128(rk, kd + i * 1024, dma_off<DQK, true>(i, lane, a.k_ss));
+        for (int i = g; i < NIO; i += NS) dma_b128(rv, vd + i * 1024, dma_off<DV, true>(i, lane, a.v_ss));
+      }
+    } else {
       const uint16_t* kr = a.k + (int64_t)b * a.k_sb + (int64_t)kc * a.k_ss + (int64_t)hkv * a.k_sh;
       const uint16_t* vr = a.v + (int64_t)b * a.v_sb + (int64_t)kc * a.v_ss + (int64_t)hkv * a.v_sh;
 #pragma unroll
@@ -395,7 +413,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void bwd_dkdv_kernel(BwdArgs a)
                                  rows * (int)a.q_ss * 2);
       const i32x4 ro = make_rsrc(a.dout + (int64_t)b * a.do_sb + (int64_t)r0 * a.do_ss + (int64_t)h * a.do_sh,
                                  rows * (int)a.do_ss * 2);
-      const uint32_t qd = smem_addr + (uint32_t)((g * 2 + s) * STAGE) * 2, od = qd + QT * 2, ldd = od + OT * 2;
+      const uint32_t qd = smem_addr + (uint32_t)(RES + (g * 2 + s) * STAGE) * 2, od = qd + QT * 2, ldd = od + OT * 2;
 #pragma unroll
       for (int j = 0; j < JQ; ++j)
         if (NIQ % NR == 0 || rw + NR * j < NIQ) dma_b128(rq, qd + (rw + NR * j) * 1024, qoff[j]);
@@ -426,7 +444,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void bwd_dkdv_kernel(BwdArgs a)
       // this wave's keys [wk0, wk0 + 32) against the block's band of rows
       if ((WIN || CAUSAL) && wk0 > off + r0 + 31 + wrgt) continue;
       if (WIN && wk0 + 31 < off + r0 - wlft) continue;
-      const uint16_t* qt = lds16 + (g * 2 + s) * STAGE;
+      const uint16_t* qt = lds16 + RES + (g * 2 + s) * STAGE;
       const uint16_t* ot = qt + QT;
       const float* lt = reinterpret_cast<const float*>(ot + OT);
       // S = Q K^T and dP = dO V^T: a lane owns a key; its registers cover rows
@@ -434,9 +452,13 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void bwd_dkdv_kernel(BwdArgs a)
       const int prow = perm32(lane & 31);
       f32x16 sc = (f32x16){}, dp = (f32x16){};
 #pragma unroll
-      for (int st = 0; st < KS; ++st) sc = T::mfma32(row_frag<DQK, true>(qt, prow, 2 * st + hh), kf[st], sc);
+      for (int st = 0; st < KS; ++st)
+        sc = T::mfma32(row_frag<DQK, true>(qt, prow, 2 * st + hh),
+                       KVL ? row_frag<DQK, true>(kres, lane & 31, 2 * st + hh) : kf[KVL ? 0 : st], sc);
 #pragma unroll
-      for (int st = 0; st < VS; ++st) dp = T::mfma32(row_frag<DV, false>(ot, prow, 2 * st + hh), vf[st], dp);
+      for (int st = 0; st < VS; ++st)
+        dp = T::mfma32(row_frag<DV, false>(ot, prow, 2 * st + hh),
+                       KVL ? row_frag<DV, true>(vres, lane & 31, 2 * st + hh) : vf[KVL ? 0 : st], dp);
       u32x4 pf[2], dsf[2];
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
@@ -474,6 +496,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void bwd_dkdv_kernel(BwdArgs a)
       }
     }
 
+    if constexpr (KVL) __builtin_amdgcn_s_waitcnt(0x0F70);   // resident copies landed before LDS is reused
     __syncthreads();
     if constexpr (NS > 1) {   // add the row-split groups' partial sums into group 0
       float* mo = reinterpret_cast<float*>(smem);
@@ -546,12 +569,12 @@ static hipError_t launch_dq(BwdArgs a, hipStream_t st) {
                      dim3(64 * NR * NS), 0, st, a);
   return hipGetLastError();
 }
-template <class T, int DQK, int DV, bool CAUSAL, bool WIN, int NR, int NS, bool PAIR, int MINW>
+template <class T, int DQK, int DV, bool CAUSAL, bool WIN, int NR, int NS, bool PAIR, int MINW, bool KVL = false>
 static hipError_t launch_dkdv(BwdArgs a, hipStream_t st) {
   a.num_tiles = (a.Sk + 32 * NR - 1) / (32 * NR);
   const int64_t units = (int64_t)a.B * a.Hkv * (PAIR ? (a.num_tiles + 1) / 2 : a.num_tiles);
   a.xcd_remap = PAIR && units % 8 == 0;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, DQK, DV, CAUSAL, WIN, NR, NS, PAIR, MINW>), dim3((unsigned)units),
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, DQK, DV, CAUSAL, WIN, NR, NS, PAIR, MINW, KVL>), dim3((unsigned)units),
                      dim3(64 * NR * NS), 0, st, a);
   return hipGetLastError();
 }
@@ -581,6 +604,8 @@ static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   if constexpr (DQK <= 64) {
     if constexpr (CAUSAL) return launch_dkdv<T, DQK, DV, CAUSAL, WIN, 2, 4, true, 2>(a, st);
     else return launch_dkdv<T, DQK, DV, CAUSAL, WIN, 4, 2, false, 2>(a, st);
+  } else if constexpr (DQK <= 128) {
+    return launch_dkdv<T, DQK, DV, CAUSAL, WIN, 4, 2, false, 2, true>(a, st);
   } else {
     return launch_dkdv<T, DQK, DV, CAUSAL, WIN, 4, 1, false, 1>(a, st);
   }
