@@ -23,6 +23,9 @@ What it computes, and where each function's definition comes from:
 * ``kvcache_ref`` -- append rotated new keys and raw new values into the cache
   at ``cache_seqlens`` and attend the rotated query over the cache prefix
   (issue #1402, both scripts; PR #99 test parametrisation).
+* ``attention_bwd_ref`` -- the gradients dQ, dK, dV (flash-attention PR #1604).
+* ``e4m3_decode``, ``attention_fp8_ref`` -- FP8 e4m3 inputs with per-tensor
+  descale factors (the skill page, Workflow 3).
 
 Pins (tests/test_oracle_pins.py) tie every function to closed forms, library
 routines, invariants the pages state, and brute force on tiny shapes.
@@ -32,8 +35,9 @@ from .attention import attention_ref, attention_varlen_ref
 from .rope import rope_ref
 from .backward import attention_bwd_ref
 from .kvcache import kvcache_ref
+from .fp8 import e4m3_decode, attention_fp8_ref
 
 __all__ = [
-    "attention_ref", "attention_varlen_ref", "attention_bwd_ref", "rope_ref", "kvcache_ref", "round_to_dtype", "dtype_bits",
+    "attention_ref", "attention_varlen_ref", "attention_bwd_ref", "e4m3_decode", "attention_fp8_ref", "rope_ref", "kvcache_ref", "round_to_dtype", "dtype_bits",
     "bits_to_f64", "to_f64", "f32_to_bf16_rne_bits",
 ]

@@ -16,7 +16,8 @@ import torch
 from scipy.special import logsumexp
 
 import workloads as W
-from oracle import (attention_bwd_ref, attention_ref, attention_varlen_ref, bits_to_f64, dtype_bits,
+from oracle import (attention_bwd_ref, attention_fp8_ref, attention_ref, attention_varlen_ref, bits_to_f64,
+                    dtype_bits, e4m3_decode,
                     f32_to_bf16_rne_bits, kvcache_ref, rope_ref, round_to_dtype, to_f64)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -542,3 +543,68 @@ def test_empty_cache_config_equals_plain_attention():
     ref, _ = attention_ref(f(case.q), f(case.k_new), f(case.v_new))
     assert np.array_equal(out, ref)
     assert np.array_equal(kc, f(case.k_new))
+
+
+# ---------------------------------------------------------------- FP8 inputs
+# The skill page "Flash Attention - Fast Memory-Efficient Attention", Workflow
+# 3: q, k, v converted to FP8 (e4m3); the decoding is pinned to torch's own
+# float8_e4m3fn conversion on all 256 codes and to hand-decoded code points.
+
+def test_e4m3_decode_matches_torch_on_every_code():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = e4m3_decode(codes.numpy())
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+@pytest.mark.parametrize("code,value", [(0x00, 0.0), (0x38, 1.0), (0x40, 2.0), (0x3C, 1.5), (0x7E, 448.0),
+                                        (0x08, 2.0 ** -6), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9),
+                                        (0xC0, -2.0), (0xB8, -1.0), (0x30, 0.5)])
+def test_e4m3_code_points(code, value):
+    assert e4m3_decode([code])[0] == value
+
+
+def test_e4m3_nan_codes_and_order():
+    vals = e4m3_decode(np.arange(256))
+    assert np.isnan(vals[0x7F]) and np.isnan(vals[0xFF]) and np.isnan(vals).sum() == 2
+    pos = vals[:0x7F]
+    assert np.all(np.diff(pos) > 0)                       # codes 0..126 increase strictly
+    assert np.array_equal(vals[0x80:0xFF], -pos)           # the sign bit only flips the sign
+    assert np.signbit(vals[0x80]) and vals[0x80] == 0.0
+
+
+def test_e4m3_round_trip_of_representable_values():
+    vals = e4m3_decode(np.arange(0x7F))
+    codes = torch.from_numpy(vals).to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, np.arange(0x7F))
+
+
+def _fp8_codes(shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_fp8_attention_is_attention_of_decoded_values():
+    q8, k8, v8 = _fp8_codes((1, 5, 2, 4), 31), _fp8_codes((1, 7, 1, 4), 32), _fp8_codes((1, 7, 1, 3), 33)
+    out, lse = attention_fp8_ref(q8, k8, v8, causal=True)
+    # brute force on the decoded values, one row at a time
+    q, k, v = e4m3_decode(q8), e4m3_decode(k8), e4m3_decode(v8)
+    for h in range(2):
+        for i in range(5):
+            s = [float(np.dot(q[0, i, h], k[0, j, 0])) / 2.0 for j in range(7) if j <= i + 2]
+            w = np.exp(np.array(s) - max(s))
+            want = (w[:, None] * v[0, :len(s), 0]).sum(0) / w.sum()
+            assert np.allclose(out[0, i, h], want, rtol=0, atol=1e-12)
+            assert abs(lse[0, h, i] - (max(s) + math.log(w.sum()))) < 1e-12
+
+
+def test_fp8_descales_enter_as_score_scale_and_output_scale():
+    q8, k8, v8 = _fp8_codes((2, 6, 4, 8), 41), _fp8_codes((2, 9, 2, 8), 42), _fp8_codes((2, 9, 2, 8), 43)
+    out, lse = attention_fp8_ref(q8, k8, v8, descale_q=0.5, descale_k=3.0, descale_v=0.25, causal=False)
+    base, base_lse = attention_ref(e4m3_decode(q8), e4m3_decode(k8), e4m3_decode(v8),
+                                   softmax_scale=1.5 / math.sqrt(8))
+    assert np.allclose(out, 0.25 * base, rtol=1e-13, atol=1e-15)
+    assert np.allclose(lse, base_lse, rtol=1e-13, atol=1e-13)
