@@ -28,6 +28,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 2516.6     # dense fp16/bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0    # HBM3E
+PEAK_FP8_TFLOPS = 5033.2  # dense fp8 MFMA (twice the fp16 rate)
+# FP8-input attention runs Q K^T in fp8 and P V in bf16 (half of the flops each)
+PEAK_FP8_BLEND = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_TFLOPS)
 METRIC = "attn prefill TFLOP/s + decode KV GB/s at 1 GPU, as % of MI355X peak"
 
 
@@ -38,7 +41,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
-                    help="comma list of extra workloads to time: decode, chunked, window, bwd, varlen, asym, empty "
+                    help="comma list of extra workloads to time: decode, chunked, window, bwd, varlen, fp8, asym, empty "
                          "(default: all; 'none' times the headline only)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -249,6 +252,21 @@ def main():
             "us": t * 1e6, "gflop": fl / 1e9, "tflops": fl / t / 1e12,
             "pct_mfma_peak": 100 * fl / t / 1e12 / PEAK_TFLOPS, "lengths": lens}
         del call, q, k, v, out, c
+
+    # ---------------- FP8 (e4m3) inputs on the headline shape, non-causal and causal
+    if want("fp8"):
+        for causal in (False, True):
+            c = W.fwd_fp8_d64(causal)
+            q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
+            out = torch.empty((2, 2048, 8, 64), dtype=torch.bfloat16, device=dev)
+            call = E.prepare_fp8(q, k, v, out, causal, None)
+            t = time_loop([call], K, Wm, torch)
+            fl = W.fwd_flops(2, 2048, 2048, 8, 64, 64, causal)
+            results["fwd_fp8_b2h8s2048d64" + ("_causal" if causal else "")] = {
+                "us": t * 1e6, "gflop": fl / 1e9, "tflops": fl / t / 1e12,
+                "pct_blended_peak": 100 * fl / t / 1e12 / PEAK_FP8_BLEND,
+                "peak_note": "QK^T on fp8 MFMA, PV on bf16 MFMA: blended peak %.0f TFLOP/s" % PEAK_FP8_BLEND}
+            del call, q, k, v, out, c
 
     # ---------------- asymmetric head dims: B=2 H=16 S=4096 Dqk=192 Dv=128 bf16 causal
     if want("asym"):

@@ -31,9 +31,10 @@ ATTN_OK = 0
 ERRORS = {-1: "ATTN_E_NULL", -2: "ATTN_E_SHAPE", -3: "ATTN_E_UNSUPPORTED", -4: "ATTN_E_ALIGN",
           -5: "ATTN_E_WORKSPACE", -6: "ATTN_E_OVERFLOW", -7: "ATTN_E_HIP"}
 EXPORTED = ["attn_fwd", "attn_fwd_varlen", "attn_fwd_kvcache", "attn_fwd_kvcache_workspace_size",
-            "attn_bwd", "attn_bwd_workspace_size", "rope_apply", "attn_validate_fwd",
-            "attn_validate_varlen", "attn_validate_kvcache", "attn_validate_bwd", "attn_validate_rope",
-            "attn_last_error", "attn_abi_version"]
+            "attn_bwd", "attn_bwd_workspace_size", "attn_fwd_fp8", "attn_fwd_fp8_workspace_size",
+            "rope_apply", "attn_validate_fwd", "attn_validate_varlen", "attn_validate_kvcache",
+            "attn_validate_bwd", "attn_validate_fp8", "attn_validate_rope", "attn_last_error",
+            "attn_abi_version"]
 
 
 class AttnError(RuntimeError):
@@ -55,6 +56,16 @@ class FwdParams(ctypes.Structure):
                 ("lse", ctypes.c_void_p), ("causal", ctypes.c_int),
                 ("softmax_scale", ctypes.c_float),
                 ("window_left", ctypes.c_int), ("window_right", ctypes.c_int)]
+
+
+class Fp8Params(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("Sq", ctypes.c_int), ("Sk", ctypes.c_int), ("Hq", ctypes.c_int),
+                ("Hkv", ctypes.c_int), ("D", ctypes.c_int),
+                ("q", Tensor4), ("k", Tensor4), ("v", Tensor4), ("out", Tensor4),
+                ("lse", ctypes.c_void_p), ("causal", ctypes.c_int), ("softmax_scale", ctypes.c_float),
+                ("descale_q", ctypes.c_float), ("descale_k", ctypes.c_float), ("descale_v", ctypes.c_float),
+                ("window_left", ctypes.c_int), ("window_right", ctypes.c_int),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class VarlenParams(ctypes.Structure):
@@ -117,10 +128,14 @@ _lib.rope_apply.argtypes = [ctypes.POINTER(RopeParams), ctypes.c_void_p]
 _lib.attn_validate_fwd.argtypes = [ctypes.POINTER(FwdParams)]
 _lib.attn_validate_kvcache.argtypes = [ctypes.POINTER(KVCacheParams)]
 _lib.attn_validate_rope.argtypes = [ctypes.POINTER(RopeParams)]
+_lib.attn_fwd_fp8.argtypes = [ctypes.POINTER(Fp8Params), ctypes.c_void_p]
+_lib.attn_validate_fp8.argtypes = [ctypes.POINTER(Fp8Params)]
+_lib.attn_fwd_fp8_workspace_size.argtypes = [ctypes.POINTER(Fp8Params)]
+_lib.attn_fwd_fp8_workspace_size.restype = ctypes.c_size_t
 _lib.attn_last_error.restype = ctypes.c_char_p
-for _n in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_kvcache", "attn_bwd", "rope_apply", "attn_validate_fwd",
-           "attn_validate_varlen", "attn_validate_kvcache", "attn_validate_bwd", "attn_validate_rope",
-           "attn_abi_version"):
+for _n in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_kvcache", "attn_bwd", "attn_fwd_fp8", "rope_apply",
+           "attn_validate_fwd", "attn_validate_varlen", "attn_validate_kvcache", "attn_validate_bwd",
+           "attn_validate_fp8", "attn_validate_rope", "attn_abi_version"):
     getattr(_lib, _n).restype = ctypes.c_int
 
 _DT = {torch.float16: 0, torch.bfloat16: 1}
@@ -224,6 +239,59 @@ def prepare_bwd(dout, q, k, v, out, lse, dq, dk, dv, causal=False, softmax_scale
     p = bwd_params(q, k, v, out, dout, lse, dq, dk, dv, causal, softmax_scale, window_size)
     ws = _bwd_workspace(p, q.device)
     return PreparedCall(_lib.attn_bwd, p, _stream(q), (dout, q, k, v, out, lse, dq, dk, dv, ws))
+
+
+# ---------------------------------------------------------------- FP8 inputs
+
+def _codes(t):
+    """e4m3 codes: a torch.float8_e4m3fn tensor or its uint8 bit pattern."""
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise AttnError(-3, "fp8 inputs must be float8_e4m3fn or uint8 codes, got %s" % t.dtype)
+    return t
+
+
+def fp8_params(q, k, v, out, causal=False, softmax_scale=None, lse=None, window_size=(-1, -1),
+               descale_q=1.0, descale_k=1.0, descale_v=1.0):
+    q, k, v = _codes(q), _codes(k), _codes(v)
+    B, Sq, Hq, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    return Fp8Params(B, Sq, Sk, Hq, Hkv, D, _t4(q), _t4(k), _t4(v), _t4(out),
+                     lse.data_ptr() if lse is not None else None, int(bool(causal)), _scale(softmax_scale),
+                     float(descale_q), float(descale_k), float(descale_v),
+                     int(window_size[0]), int(window_size[1]), None, 0)
+
+
+def _fp8_workspace(p, device):
+    need = int(_lib.attn_fwd_fp8_workspace_size(ctypes.byref(p)))
+    ws = torch.empty(need + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    p.workspace = ws.data_ptr() + off if need else None
+    p.workspace_bytes = need
+    return ws
+
+
+def attn_fwd_fp8(q, k, v, causal=False, softmax_scale=None, out=None, return_lse=False,
+                 window_size=(-1, -1), descale_q=1.0, descale_k=1.0, descale_v=1.0):
+    """Exact attention of e4m3 inputs (float8_e4m3fn or uint8 codes) q [B,Sq,Hq,D],
+    k, v [B,Sk,Hkv,D], each element times its tensor's descale; out [B,Sq,Hq,D] bf16."""
+    B, Sq, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
+    p = fp8_params(q, k, v, out, causal, softmax_scale, lse, window_size, descale_q, descale_k, descale_v)
+    ws = _fp8_workspace(p, q.device)
+    _check(_lib.attn_fwd_fp8(ctypes.byref(p), _stream(q)))
+    del ws
+    return (out, lse) if return_lse else out
+
+
+def prepare_fp8(q, k, v, out, causal=False, softmax_scale=None, lse=None, window_size=(-1, -1),
+                descale_q=1.0, descale_k=1.0, descale_v=1.0):
+    p = fp8_params(q, k, v, out, causal, softmax_scale, lse, window_size, descale_q, descale_k, descale_v)
+    ws = _fp8_workspace(p, q.device)
+    return PreparedCall(_lib.attn_fwd_fp8, p, _stream(q), (q, k, v, out, lse, ws))
 
 
 # ---------------------------------------------------------------- packed sequences
@@ -398,5 +466,5 @@ __all__ = ["PreparedCall", "prepare_fwd", "prepare_varlen", "prepare_kvcache", "
            "BwdParams", "bwd_params", "attn_fwd", "attn_fwd_varlen",
            "attn_fwd_kvcache", "rope_apply", "kvcache_workspace_size", "AttnError",
            "FwdParams", "VarlenParams", "KVCacheParams", "RopeParams", "Tensor4", "fwd_params",
-           "varlen_params", "kvcache_params",
+           "varlen_params", "kvcache_params", "Fp8Params", "fp8_params", "attn_fwd_fp8", "prepare_fp8",
            "rope_params", "lib", "EXPORTED", "LIB_PATH"]

@@ -333,9 +333,57 @@ void set_t(uint16_t*& ptr, int64_t& sb, int64_t& ss, int64_t& sh, const attn_ten
   ptr = static_cast<uint16_t*>(t.data); sb = t.stride_b; ss = t.stride_s; sh = t.stride_h;
 }
 
+int check_fp8_tensor(const attn_tensor4& t, const char* name) {
+  if (!t.data) return fail(ATTN_E_NULL, "%s: data pointer is NULL", name);
+  if (reinterpret_cast<uintptr_t>(t.data) % 16)
+    return fail(ATTN_E_ALIGN, "%s: data pointer is not 16-byte aligned", name);
+  if (t.stride_b % 16 || t.stride_s % 16 || t.stride_h % 16)
+    return fail(ATTN_E_ALIGN, "%s: strides (%lld, %lld, %lld) of a 1-byte tensor must be multiples of 16", name,
+                (long long)t.stride_b, (long long)t.stride_s, (long long)t.stride_h);
+  if (t.stride_b < 0 || t.stride_s < 0 || t.stride_h < 0)
+    return fail(ATTN_E_SHAPE, "%s: negative stride", name);
+  return ATTN_OK;
+}
+
+size_t fp8_workspace(const attn_fp8_params* p) {
+  if (!p || p->B < 0 || p->Sk < 0 || p->Hkv < 1 || p->D < 0) return 0;
+  return align_up((size_t)p->B * p->Sk * p->Hkv * p->D * 2);
+}
+
+int validate_fp8(const attn_fp8_params* p) {
+  if (!p) return fail(ATTN_E_NULL, "params pointer is NULL");
+  int e;
+  if (p->B < 0 || p->Sq < 0 || p->Sk < 0 || p->Hq < 1 || p->Hkv < 1)
+    return fail(ATTN_E_SHAPE, "sizes must satisfy B, Sq, Sk >= 0 and Hq, Hkv >= 1");
+  if (p->Sq >= attn::kNoWindow || p->Sk >= attn::kNoWindow)
+    return fail(ATTN_E_SHAPE, "sequence lengths must be below 2^29");
+  if (p->Hq % p->Hkv)
+    return fail(ATTN_E_SHAPE, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+  if (p->D != 64 && p->D != 128)
+    return fail(ATTN_E_UNSUPPORTED, "fp8 head size %d is not 64 or 128", p->D);
+  if (p->window_left < -1 || p->window_right < -1)
+    return fail(ATTN_E_SHAPE, "window (%d, %d): each side must be >= -1", p->window_left, p->window_right);
+  if (!std::isfinite(p->descale_q) || !std::isfinite(p->descale_k) || !std::isfinite(p->descale_v))
+    return fail(ATTN_E_SHAPE, "descale factors must be finite");
+  if (p->B == 0 || p->Sq == 0) return ok();
+  if ((e = check_fp8_tensor(p->q, "q"))) return e;
+  if (p->Sk > 0) {
+    if ((e = check_fp8_tensor(p->k, "k"))) return e;
+    if ((e = check_fp8_tensor(p->v, "v"))) return e;
+    const size_t need = fp8_workspace(p);
+    if (!p->workspace || p->workspace_bytes < need)
+      return fail(ATTN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  p->workspace ? p->workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(p->workspace) % kAlign)
+      return fail(ATTN_E_ALIGN, "workspace must be 256-byte aligned");
+  }
+  if ((e = check_tensor(p->out, "out"))) return e;
+  return ok();
+}
+
 extern "C" {
 
-int attn_abi_version(void) { return 2; }
+int attn_abi_version(void) { return 3; }
 
 const char* attn_last_error(void) { return g_err.c_str(); }
 
@@ -343,6 +391,7 @@ int attn_validate_fwd(const attn_fwd_params* p) { return validate_fwd(p); }
 int attn_validate_kvcache(const attn_kvcache_params* p) { return validate_kvcache(p); }
 int attn_validate_varlen(const attn_varlen_params* p) { return validate_varlen(p); }
 int attn_validate_bwd(const attn_bwd_params* p) { return validate_bwd(p); }
+int attn_validate_fp8(const attn_fp8_params* p) { return validate_fp8(p); }
 int attn_validate_rope(const attn_rope_params* p) { return validate_rope(p); }
 
 int attn_fwd(const attn_fwd_params* p, void* stream) {
@@ -403,6 +452,35 @@ int attn_fwd_varlen(const attn_varlen_params* p, void* stream) {
   if (p->max_seqlen_q == 0) return ok();
   hipError_t he = attn::run_tile_attn(a, p->dtype == ATTN_DTYPE_BF16, p->Dqk, p->Dv, p->causal != 0, st);
   if (he != hipSuccess) return hip_fail(he, "attn_fwd_varlen launch");
+  return ok();
+}
+
+size_t attn_fwd_fp8_workspace_size(const attn_fp8_params* p) { return fp8_workspace(p); }
+
+int attn_fwd_fp8(const attn_fp8_params* p, void* stream) {
+  int e = validate_fp8(p);
+  if (e) return e;
+  if (p->B == 0 || p->Sq == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  attn::AttnArgs a = base_args();
+  set_q(a, p->q); set_k(a, p->k); set_o(a, p->out);
+  if (p->Sk > 0) {
+    // v as bf16, contiguous [B, Sk, Hkv, D]
+    hipError_t he = attn::run_e4m3_to_bf16(p->v.data, p->v.stride_b, p->v.stride_s, p->v.stride_h, p->workspace,
+                                           p->B, p->Sk, p->Hkv, p->D, st);
+    if (he != hipSuccess) return hip_fail(he, "attn_fwd_fp8 v conversion");
+    a.v = static_cast<const uint16_t*>(p->workspace);
+    a.v_ss = (int64_t)p->Hkv * p->D; a.v_sb = a.v_ss * p->Sk; a.v_sh = p->D;
+  }
+  a.lse = p->lse;
+  a.lse_sb = (int64_t)p->Hq * p->Sq; a.lse_sh = p->Sq;
+  a.B = p->B; a.Sq = p->Sq; a.Sk = p->Sk; a.Hq = p->Hq; a.Hkv = p->Hkv; a.group = p->Hq / p->Hkv;
+  a.causal = p->causal ? 1 : 0;
+  set_window(a, p->window_left, p->window_right);
+  a.c = resolve_c(p->softmax_scale, p->D) * p->descale_q * p->descale_k;
+  a.oscale = p->descale_v;
+  hipError_t he = attn::run_tile_attn_fp8(a, p->D, p->causal != 0, st);
+  if (he != hipSuccess) return hip_fail(he, "attn_fwd_fp8 launch");
   return ok();
 }
 

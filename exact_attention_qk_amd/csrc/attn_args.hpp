@@ -27,6 +27,7 @@ struct AttnArgs {
   int num_qtiles;             // tiled kernel: ceil(Sq / rows per workgroup)
   int xcd_remap;              // tiled kernel: 1 when the grid is a multiple of 8
   float c;                    // softmax_scale * log2(e)
+  float oscale;               // FP8 inputs: the descale of v, applied to the output
   // split-KV decode
   int split_len, num_splits;
   float* ws_o;                // [B, Hkv, num_splits, R, Dv] fp32 partial numerators

@@ -74,17 +74,22 @@ __device__ __forceinline__ float dot2_sum<BF16>(uint32_t p, float acc) {
                                          (bf16x2){(__bf16)1.f, (__bf16)1.f}, acc, false);
 }
 
+// F8: q and k hold e4m3 codes (1 byte per element, strides in bytes) and S^T
+// runs on the 32x32x64 fp8 MFMA; V, P and the output stay 16-bit (T).
 template <class T, int DQK, int DV, bool CAUSAL, bool WIN, int RB, int NR, int NS, int BN, bool PAIR,
-          bool FASTC, int MINW>
+          bool FASTC, int MINW, bool F8>
 __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs a) {
   constexpr int NKB = BN / 32;                           // 32-key MFMA blocks per tile
   constexpr int RW = 32 * RB;
   constexpr int BM = NR * RW;
-  constexpr int CK = DQK / 8;
+  constexpr int EK = F8 ? 1 : 2;                         // bytes per q / k element
+  constexpr int CK = DQK * EK / 16;                      // 16-byte chunks per K row
   constexpr int CV = DV / 8;
   constexpr int KSTEPS = DQK / 16;
+  constexpr int K8 = DQK / 64;                           // fp8 MFMA steps of S
+  static_assert(!F8 || DQK % 64 == 0, "fp8 head size");
   constexpr int DVB = (DV + 31) / 32;
-  constexpr int KT = BN * DQK;
+  constexpr int KT = BN * DQK * EK / 2;                  // K tile, in 16-bit LDS words
   constexpr int VT = BN * DV;
   constexpr int STAGE = KT + VT;                          // elements
   constexpr int LDS_KV = NS * 2 * STAGE * 2;              // bytes
@@ -169,7 +174,9 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
   if (WIN) wkbeg = max(0, pmin - wlft);
 
   const uint16_t* qbase = a.q + (int64_t)b * a.q_sb + (int64_t)qst * a.q_ss + (int64_t)hq * a.q_sh;
-  const uint16_t* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)kst * a.k_ss + (int64_t)hkv * a.k_sh;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) +
+                         ((int64_t)b * a.k_sb + (int64_t)kst * a.k_ss + (int64_t)hkv * a.k_sh) * EK;
+  const int64_t kss = a.k_ss * EK;                       // bytes between key rows
   const uint16_t* vbase = a.v + (int64_t)b * a.v_sb + (int64_t)kst * a.v_ss + (int64_t)hkv * a.v_sh;
 
   // ---- tile DMA: tile t of this group into stage s.  Each lane's source row
@@ -186,7 +193,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
   for (int j = 0; j < JK; ++j) {
     const int P = (rw + j * NR) * 64 + lane;
     const int row = P / CK, pos = P % CK;
-    koff_j[j] = row * a.k_ss * 2 + ((pos ^ swz_k<CK>(row)) << 4);
+    koff_j[j] = row * kss + ((pos ^ swz_k<CK>(row)) << 4);
   }
 #pragma unroll
   for (int j = 0; j < JV; ++j) {
@@ -199,7 +206,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
     const uint32_t vd = kd + KT * 2;
     const int key0 = t * BN;
     const int rows = min(BN, L - key0);
-    const i32x4 rk = make_rsrc(kbase + (int64_t)key0 * a.k_ss, rows * a.k_ss * 2);
+    const i32x4 rk = make_rsrc(kbase + (int64_t)key0 * kss, rows * kss);
     const i32x4 rv = make_rsrc(vbase + (int64_t)key0 * a.v_ss, rows * a.v_ss * 2);
 #pragma unroll
     for (int j = 0; j < JK; ++j) {
@@ -215,14 +222,28 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
     }
   };
 
-  // ---- Q fragments (B operand of S^T = K Q^T)
-  u32x4 qf[RB][KSTEPS];
+  // ---- Q fragments (B operand of S^T = K Q^T); fp8: 32 bytes per lane and
+  // 64 dims, the same dims as the lane's K fragment (any order works as long
+  // as both operands use it)
+  u32x4 qf[RB][F8 ? 1 : KSTEPS];
+  i32x8 q8[RB][F8 ? K8 : 1];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int qrow = wr0 + rb * 32 + (lane & 31);
     const int qr = min(qrow, Sqb - 1);
+    if constexpr (F8) {
+      const uint8_t* qb = reinterpret_cast<const uint8_t*>(a.q) + (int64_t)b * a.q_sb + (int64_t)(qst + qr) * a.q_ss +
+                          (int64_t)hq * a.q_sh;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[rb][s] = ldg16(qbase + (int64_t)qr * a.q_ss + 16 * s + 8 * hh);
+      for (int s = 0; s < K8; ++s) {
+        const u32x4 lo = ldg16(qb + 64 * s + 32 * hh), hi = ldg16(qb + 64 * s + 32 * hh + 16);
+        q8[rb][s] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                            (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qf[rb][s] = ldg16(qbase + (int64_t)qr * a.q_ss + 16 * s + 8 * hh);
+    }
   }
 
   f32x16 o[RB][DVB];
@@ -266,14 +287,30 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
       blk_on[kb] = key0 + kb * 32 < wkend && (!WIN || key0 + kb * 32 + 32 > wkbeg);
       if (blk_on[kb]) {
         const int krow = kb * 32 + key_perm(lane & 31);
-        const uint16_t* kr = kt + krow * DQK;
         const int sw = swz_k<CK>(krow);
+        if constexpr (F8) {
+          const uint8_t* kr = reinterpret_cast<const uint8_t*>(kt) + krow * DQK;
 #pragma unroll
-        for (int st = 0; st < KSTEPS; ++st) {
-          const u32x4 af = *reinterpret_cast<const u32x4*>(kr + (((2 * st + hh) ^ sw) << 3));
+          for (int st = 0; st < K8; ++st) {
+            const int c0 = 4 * st + 2 * hh;
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(kr + ((c0 ^ sw) << 4));
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(kr + (((c0 + 1) ^ sw) << 4));
+            const i32x8 af = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            sc[rb][kb] = T::mfma32(af, qf[rb][st], st == 0 ? (f32x16){} : sc[rb][kb]);
+            for (int rb = 0; rb < RB; ++rb)
+              sc[rb][kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  af, q8[rb][st], st == 0 ? (f32x16){} : sc[rb][kb], 0, 0, 0, 0, 0, 0);
+          }
+        } else {
+          const uint16_t* kr = kt + krow * DQK;
+#pragma unroll
+          for (int st = 0; st < KSTEPS; ++st) {
+            const u32x4 af = *reinterpret_cast<const u32x4*>(kr + (((2 * st + hh) ^ sw) << 3));
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              sc[rb][kb] = T::mfma32(af, qf[rb][st], st == 0 ? (f32x16){} : sc[rb][kb]);
+          }
         }
       } else {
 #pragma unroll
@@ -423,6 +460,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
     for (int rb = 0; rb < RB; ++rb) {
       lsum[rb] = xhalf_sum(l_run[rb]);
       inv[rb] = lsum[rb] > 0.f ? 1.f / lsum[rb] : 0.f;
+      if constexpr (F8) inv[rb] *= a.oscale;
     }
     uint16_t* lds_o = lds16 + rw * RW * OSTR;
 #pragma unroll
@@ -469,7 +507,8 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
 }
 
 // ---------------------------------------------------------------- launchers
-template <class T, int DQK, int DV, bool CAUSAL, bool WIN, int RB, int NR, int NS, int BN, bool PAIR, int MINW>
+template <class T, int DQK, int DV, bool CAUSAL, bool WIN, int RB, int NR, int NS, int BN, bool PAIR, int MINW,
+          bool F8>
 static hipError_t launch_cfg(const AttnArgs& a0, bool fastc, hipStream_t st) {
   AttnArgs a = a0;
   constexpr int BM = NR * 32 * RB;
@@ -479,39 +518,39 @@ static hipError_t launch_cfg(const AttnArgs& a0, bool fastc, hipStream_t st) {
   a.xcd_remap = (units % 8 == 0) ? 1 : 0;
   const dim3 grid((unsigned)units), block(64 * NR * NS);
   if (fastc)
-    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, WIN, RB, NR, NS, BN, PAIR, true, MINW>), grid,
+    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, WIN, RB, NR, NS, BN, PAIR, true, MINW, F8>), grid,
                        block, 0, st, a);
   else
-    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, WIN, RB, NR, NS, BN, PAIR, false, MINW>), grid,
+    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, WIN, RB, NR, NS, BN, PAIR, false, MINW, F8>), grid,
                        block, 0, st, a);
   return hipGetLastError();
 }
 
 // Rows per workgroup and key splits per head dimension: small problems get
 // key-split groups so that every CU runs several waves.
-template <class T, int DQK, int DV, bool CAUSAL, bool WIN>
+template <class T, int DQK, int DV, bool CAUSAL, bool WIN, bool F8 = false>
 static hipError_t launch_dims(const AttnArgs& a, bool fastc, hipStream_t st) {
   const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
   if constexpr (DQK <= 16) {
-    return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 1, 64, false, 2>(a, fastc, st);
+    return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 1, 64, false, 2, F8>(a, fastc, st);
   } else if constexpr (DQK <= 64) {
-    if (CAUSAL) return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 2, 4, 32, true, 2>(a, fastc, st);
-    if (rows <= 256 * 256) return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 2, 64, false, 2>(a, fastc, st);
-    return launch_cfg<T, DQK, DV, CAUSAL, WIN, 2, 2, 2, 64, false, 2>(a, fastc, st);
+    if (CAUSAL) return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 2, 4, 32, true, 2, F8>(a, fastc, st);
+    if (rows <= 256 * 256) return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 2, 64, false, 2, F8>(a, fastc, st);
+    return launch_cfg<T, DQK, DV, CAUSAL, WIN, 2, 2, 2, 64, false, 2, F8>(a, fastc, st);
   } else {
     // one query block per wave keeps two waves per SIMD at these head sizes
-    return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 1, 64, false, 2>(a, fastc, st);
+    return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 1, 64, false, 2, F8>(a, fastc, st);
   }
 }
 
-template <class T, int DQK, int DV>
+template <class T, int DQK, int DV, bool F8 = false>
 static hipError_t launch_tile_c(const AttnArgs& a, bool causal, bool fastc, hipStream_t st) {
   const bool win = a.wl < kNoWindow || a.wr < kNoWindow;
   if (win)
-    return causal ? launch_dims<T, DQK, DV, true, true>(a, fastc, st)
-                  : launch_dims<T, DQK, DV, false, true>(a, fastc, st);
-  return causal ? launch_dims<T, DQK, DV, true, false>(a, fastc, st)
-                : launch_dims<T, DQK, DV, false, false>(a, fastc, st);
+    return causal ? launch_dims<T, DQK, DV, true, true, F8>(a, fastc, st)
+                  : launch_dims<T, DQK, DV, false, true, F8>(a, fastc, st);
+  return causal ? launch_dims<T, DQK, DV, true, false, F8>(a, fastc, st)
+                : launch_dims<T, DQK, DV, false, false, F8>(a, fastc, st);
 }
 
 template <class T>
@@ -528,6 +567,60 @@ hipError_t run_tile_attn(const AttnArgs& a, int dtype_bf16, int dqk, int dv, boo
   const bool fastc = a.c > 0.f;
   return dtype_bf16 ? launch_tile_t<BF16>(a, dqk, dv, causal, fastc, st)
                     : launch_tile_t<F16>(a, dqk, dv, causal, fastc, st);
+}
+
+hipError_t run_tile_attn_fp8(const AttnArgs& a, int d, bool causal, hipStream_t st) {
+  const bool fastc = a.c > 0.f;
+  if (d == 64) return launch_tile_c<BF16, 64, 64, true>(a, causal, fastc, st);
+  if (d == 128) return launch_tile_c<BF16, 128, 128, true>(a, causal, fastc, st);
+  return hipErrorInvalidValue;
+}
+
+// One e4m3 code (bits 0..7) as bf16 bits, exactly: normal numbers move their
+// exponent from bias 7 to bias 127 and their 3 mantissa bits to the top of
+// bf16's 7; subnormals m * 2^-9 (m = 1..7) are normal in bf16; S.1111.111 is
+// NaN.  Integer operations only.
+__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
+  const uint32_t sign = (c & 0x80u) << 8, e = (c >> 3) & 0xFu, m = c & 0x7u;
+  uint32_t mag;
+  if (e == 0) {
+    mag = m ? (__builtin_bit_cast(uint32_t, (float)m * 0.001953125f) >> 16) : 0u;   // m * 2^-9
+  } else if (e == 0xFu && m == 0x7u) {
+    mag = 0x7FC0u;
+  } else {
+    mag = ((e + 120u) << 7) | (m << 4);
+  }
+  return sign | mag;
+}
+
+// e4m3 codes -> bf16, [B, S, H, D] with byte strides -> contiguous [B, S, H, D].
+// A lane converts 8 elements.
+__global__ __launch_bounds__(256) void e4m3_to_bf16_kernel(const uint8_t* src, int64_t sb, int64_t ss, int64_t sh,
+                                                           uint16_t* dst, int B, int S, int H, int D) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int CH = D / 8;
+  const int64_t total = (int64_t)B * S * H * CH;
+  if (i >= total) return;
+  const int ch = (int)(i % CH);
+  const int64_t r = i / CH;
+  const int h = (int)(r % H), s = (int)((r / H) % S), b = (int)(r / ((int64_t)H * S));
+  const u32x2 w = *reinterpret_cast<const u32x2*>(src + (int64_t)b * sb + (int64_t)s * ss + (int64_t)h * sh + ch * 8);
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t word = w[j >> 1] >> (16 * (j & 1));
+    o[j] = e4m3_to_bf16_bits(word & 0xFFu) | (e4m3_to_bf16_bits((word >> 8) & 0xFFu) << 16);
+  }
+  stg16(dst + r * D + ch * 8, (u32x4){o[0], o[1], o[2], o[3]});
+}
+
+hipError_t run_e4m3_to_bf16(const void* src, int64_t sb, int64_t ss, int64_t sh, void* dst, int B, int S, int H,
+                            int D, hipStream_t st) {
+  const int64_t total = (int64_t)B * S * H * (D / 8);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(e4m3_to_bf16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const uint8_t*>(src), sb, ss, sh, static_cast<uint16_t*>(dst), B, S, H, D);
+  return hipGetLastError();
 }
 
 }  // namespace attn

@@ -1,7 +1,7 @@
 /*
  * attn.h -- C ABI of the MI355X (gfx950) exact-attention library (libattn.so).
  *
- * Three operations, named after the functions the pages discuss:
+ * The operations, named after the functions the pages discuss:
  *
  *   attn_fwd          exact attention softmax(scale * Q K^T + mask) V computed
  *                     tile by tile with an online softmax, so the score matrix
@@ -52,7 +52,8 @@
  *   message describing the last failure of the calling thread.
  * - Supported: dtype fp16 or bf16 (outputs in the input dtype, accumulation
  *   in fp32); (Dqk, Dv) in {(16,16), (64,64), (128,128), (192,128)};
- *   Hq a multiple of Hkv (q head h reads kv head h / (Hq/Hkv)).
+ *   Hq a multiple of Hkv (q head h reads kv head h / (Hq/Hkv)).  attn_fwd_fp8
+ *   takes e4m3 inputs instead (its own section below).
  * - softmax_scale: a NaN value selects 1/sqrt(Dqk); any other value,
  *   zero included, is used as given.
  */
@@ -209,6 +210,43 @@ typedef struct attn_kvcache_params {
 size_t attn_fwd_kvcache_workspace_size(const attn_kvcache_params* p);
 int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream);
 
+/* ------------------------------------------------------------- attn_fwd_fp8
+ * attn_fwd on FP8 inputs: the skill page "Flash Attention - Fast
+ * Memory-Efficient Attention", Workflow 3 (H100 FP8 optimization with
+ * FlashAttention-3) converts q, k and v to FP8 and runs attention on them.
+ * q, k, v hold e4m3 codes in the "fn" form (1 sign, 4 exponent bits with bias
+ * 7, 3 mantissa bits, no infinities, S.1111.111 = NaN); element x stands for
+ * decode(x) * descale_q (resp. descale_k, descale_v).  The result is attn_fwd
+ * of those values: out = softmax(scale * Q K^T + mask) V.
+ * q   [B, Sq, Hq,  D]  1-byte elements, read
+ * k   [B, Sk, Hkv, D]  1-byte elements, read
+ * v   [B, Sk, Hkv, D]  1-byte elements, read
+ *     (strides in elements = bytes, multiples of 16; pointers 16-byte aligned)
+ * out [B, Sq, Hq,  D]  bf16, written (strides multiples of 8 elements)
+ * lse [B, Hq, Sq] fp32 or NULL: as attn_fwd, of the descaled scores.
+ * D in {64, 128}.  causal, softmax_scale (NaN = 1/sqrt(D)) and the window
+ * as in attn_fwd.  descale_*: finite (ATTN_E_SHAPE otherwise).
+ * Arithmetic: Q K^T on the fp8 matrix cores with fp32 accumulation (exact
+ * products); v is converted to bf16 (exactly) in the workspace; the weights
+ * P are rounded to bf16 for the P V product, whose sums are fp32.
+ * workspace: attn_fwd_fp8_workspace_size(p) bytes, 256-byte aligned,
+ *     scratch (may be NULL when that size is 0).
+ */
+typedef struct attn_fp8_params {
+  int B, Sq, Sk, Hq, Hkv, D;
+  attn_tensor4 q, k, v, out;
+  float* lse;
+  int causal;
+  float softmax_scale;
+  float descale_q, descale_k, descale_v;
+  int window_left, window_right;
+  void* workspace;
+  size_t workspace_bytes;
+} attn_fp8_params;
+
+size_t attn_fwd_fp8_workspace_size(const attn_fp8_params* p);
+int attn_fwd_fp8(const attn_fp8_params* p, void* stream);
+
 /* ----------------------------------------------------------------- attn_bwd
  * Gradients of attn_fwd (flash-attention PR #1604 "Support hdimQK != hdimV
  * backward": dQ, dK, dV with head_dim_qk != head_dim_v).  For the forward
@@ -270,9 +308,10 @@ int attn_validate_fwd(const attn_fwd_params* p);
 int attn_validate_kvcache(const attn_kvcache_params* p);
 int attn_validate_varlen(const attn_varlen_params* p);
 int attn_validate_bwd(const attn_bwd_params* p);
+int attn_validate_fp8(const attn_fp8_params* p);
 int attn_validate_rope(const attn_rope_params* p);
 const char* attn_last_error(void);
-int attn_abi_version(void);  /* 2 */
+int attn_abi_version(void);  /* 3 */
 
 #ifdef __cplusplus
 }

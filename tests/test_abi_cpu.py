@@ -34,7 +34,7 @@ def test_header_functions_are_all_exported():
     lib = ctypes.CDLL(E.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert E.lib().attn_abi_version() == 2
+    assert E.lib().attn_abi_version() == 3
 
 
 def test_single_hip_runtime_in_process():
@@ -126,6 +126,32 @@ def test_validate_bwd():
     p.workspace, p.workspace_bytes = ws.data_ptr() + (-ws.data_ptr()) % 256, need
     p.lse = None
     assert E.lib().attn_validate_bwd(ctypes.byref(p)) == -1
+
+
+def test_validate_fp8():
+    q8 = torch.zeros(2, 8, 4, 64, dtype=torch.uint8)
+    k8 = torch.zeros(2, 8, 2, 64, dtype=torch.uint8)
+    out = _t((2, 8, 4, 64), torch.bfloat16)
+    p = E.fp8_params(q8, k8, k8, out)
+    assert E.lib().attn_validate_fp8(ctypes.byref(p)) == -5          # workspace missing
+    need = E.lib().attn_fwd_fp8_workspace_size(ctypes.byref(p))
+    assert need == ((2 * 8 * 2 * 64 * 2 + 255) // 256) * 256          # v as bf16
+    ws = torch.zeros(need + 512, dtype=torch.uint8)
+    p.workspace, p.workspace_bytes = ws.data_ptr() + (-ws.data_ptr()) % 256, need
+    assert E.lib().attn_validate_fp8(ctypes.byref(p)) == 0
+    p.D = 192
+    assert E.lib().attn_validate_fp8(ctypes.byref(p)) == -3          # head sizes 64 and 128 only
+    p.D = 64
+    p.descale_v = float("inf")
+    assert E.lib().attn_validate_fp8(ctypes.byref(p)) == -2
+    p.descale_v = 1.0
+    p.k.stride_s = 8                                                 # 1-byte rows: strides x16
+    assert E.lib().attn_validate_fp8(ctypes.byref(p)) == -4
+    p = E.fp8_params(q8, k8, k8, out)
+    p.workspace, p.workspace_bytes = ws.data_ptr() + (-ws.data_ptr()) % 256 + 16, need
+    assert E.lib().attn_validate_fp8(ctypes.byref(p)) == -4          # workspace alignment
+    with pytest.raises(AttnError):
+        E.fp8_params(_t((2, 8, 4, 64)), k8, k8, out)                 # not e4m3 codes
 
 
 def test_binding_rejects_other_dtypes_before_any_launch():

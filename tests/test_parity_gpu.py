@@ -12,8 +12,8 @@ import pytest
 import torch
 
 import workloads as W
-from oracle import (attention_bwd_ref, attention_ref, attention_varlen_ref, dtype_bits, kvcache_ref,
-                    rope_ref, to_f64)
+from oracle import (attention_bwd_ref, attention_fp8_ref, attention_ref, attention_varlen_ref, dtype_bits,
+                    kvcache_ref, rope_ref, to_f64)
 
 pytestmark = pytest.mark.gpu
 TOL = {"fp16": 2e-3, "bf16": 1.5e-2}
@@ -531,3 +531,82 @@ def test_rope_apply_bit_exact(dtype, interleaved, D, rd):
     ref = rope_ref(to_f64(x), to_f64(cos), to_f64(sin), 5 + np.tile(np.arange(50), (3, 1)),
                    rotary_dim=rd, interleaved=interleaved, dtype=dtype)
     assert _bits_equal(xd, ref, dtype)
+
+
+# ---------------------------------------------------------------- FP8 inputs
+# The skill page "Flash Attention - Fast Memory-Efficient Attention",
+# Workflow 3: e4m3 q, k, v with per-tensor descales.  The output is bf16, so
+# the bf16 bars apply (the weights P are rounded to bf16 for P V).
+
+def _fp8_check(case, window=(-1, -1), sample_rows=None, views=False):
+    q8, k8, v8 = dev(case.q), dev(case.k), dev(case.v)
+    if views:   # [B, H, S, D] storage seen as [B, S, H, D] (strided views)
+        q8, k8, v8 = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (q8, k8, v8))
+    B, Sq, Hq, D = q8.shape
+    buf, out = guarded_empty((B, Sq, Hq, D), torch.bfloat16)
+    dq, dk, dvs = case.descale
+    _, lse = E().attn_fwd_fp8(q8, k8, v8, causal=case.causal, softmax_scale=case.softmax_scale, out=out,
+                              return_lse=True, window_size=window, descale_q=dq, descale_k=dk, descale_v=dvs)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf, out.numel())
+    qc, kc, vc = case.q.numpy(), case.k.numpy(), case.v.numpy()
+    got, l = out, lse.cpu().double().numpy()
+    if sample_rows is not None:
+        rows = np.asarray(sample_rows)
+        qc = qc[:, rows]
+        got, l = out[:, torch.as_tensor(rows, device=DEV)], l[:, :, rows]
+    kw = dict(descale_q=dq, descale_k=dk, descale_v=dvs, causal=case.causal, softmax_scale=case.softmax_scale,
+              window=window)
+    if sample_rows is None:
+        ref, rlse = attention_fp8_ref(qc, kc, vc, **kw)
+    else:   # the sampled rows keep their positions in the full sequence
+        Sk = kc.shape[1]
+        from oracle import e4m3_decode
+        pos = np.tile(rows + Sk - Sq, (B, 1))
+        ref, rlse = attention_ref(e4m3_decode(qc) * dq, e4m3_decode(kc) * dk, e4m3_decode(vc) * dvs,
+                                  causal=case.causal, softmax_scale=case.softmax_scale, q_pos=pos, window=window)
+    err = maxabs(got, ref)
+    assert err <= TOL["bf16"], "max abs err %.3e" % err
+    fin = np.isfinite(rlse)
+    assert np.array_equal(fin, np.isfinite(l))
+    if fin.any():
+        assert np.max(np.abs(l[fin] - rlse[fin])) < LSE_TOL["bf16"]
+    return err
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_multi_tile_ragged_gqa(d, causal):
+    # 200 rows / 333 keys: several query and key tiles with ragged tails; GQA 4:2
+    _fp8_check(W.random_fp8(2, 200, 333, 4, 2, d, causal, seed=d + causal))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_descales(d):
+    _fp8_check(W.random_fp8(1, 130, 130, 2, 1, d, True, seed=5, descale=(0.5, 3.0, 1.5)))
+
+
+@pytest.mark.parametrize("sq,sk", [(100, 300), (300, 77), (1, 129)])
+def test_fp8_sq_ne_sk(sq, sk):
+    _fp8_check(W.random_fp8(1, sq, sk, 4, 4, 64, True, seed=sq))
+
+
+def test_fp8_window_and_scale():
+    _fp8_check(W.random_fp8(1, 300, 300, 2, 2, 64, True, seed=9, softmax_scale=0.2), window=(64, 16))
+
+
+def test_fp8_strided_views():
+    _fp8_check(W.random_fp8(2, 96, 96, 4, 2, 128, False, seed=11), views=True)
+
+
+def test_fp8_no_keys_gives_zero_rows():
+    case = W.random_fp8(1, 5, 0, 2, 2, 64, False, seed=1)
+    out, lse = E().attn_fwd_fp8(dev(case.q), dev(case.k), dev(case.v), return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_workload_fwd_fp8_d64_full(causal):
+    # the bench configuration: B=2, H=8, S=2048, D=64, every output row
+    _fp8_check(W.fwd_fp8_d64(causal))

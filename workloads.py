@@ -180,6 +180,35 @@ def random_fwd(B, Sq, Sk, Hq, Hkv, Dqk, Dv, dtype, causal, seed=0,
 
 
 @dataclass
+class Fp8Case:
+    """Inputs for ``attn_fwd_fp8``: e4m3 codes (uint8) q [B,Sq,Hq,D], k, v [B,Sk,Hkv,D]."""
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    causal: bool
+    descale: tuple = (1.0, 1.0, 1.0)
+    softmax_scale: float | None = None
+
+
+def _e4m3_codes(g, shape):
+    """N(0,1) draws in fp32, rounded to e4m3 (torch's float8_e4m3fn cast, RNE), as uint8 codes."""
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def random_fp8(B, Sq, Sk, Hq, Hkv, D, causal, seed=0, descale=(1.0, 1.0, 1.0), softmax_scale=None) -> Fp8Case:
+    g = torch.Generator().manual_seed(seed)
+    q = _e4m3_codes(g, (B, Sq, Hq, D))
+    k = _e4m3_codes(g, (B, Sk, Hkv, D))
+    v = _e4m3_codes(g, (B, Sk, Hkv, D))
+    return Fp8Case(q, k, v, causal, tuple(descale), softmax_scale)
+
+
+def fwd_fp8_d64(causal: bool, seed: int = 0) -> Fp8Case:
+    """The headline attn_fwd shape (B=2, H=8, S=2048, D=64) with e4m3 inputs."""
+    return random_fp8(2, 2048, 2048, 8, 8, 64, causal, seed=seed)
+
+
+@dataclass
 class VarlenCase:
     """Packed sequences: q [total_q,Hq,Dqk], k/v [total_k,Hkv,D*], cu_seqlens int32 [B+1]."""
     name: str
