@@ -374,13 +374,18 @@ def test_kvcache_chunk_window(window):
     _kv_check(case, window=window)
 
 
-def test_window_wide_equals_no_window_bitwise():
+def test_window_wide_equals_no_window():
+    # a window wider than the sequence is full attention; the two calls may
+    # use different tile shapes (so a different summation order), hence the
+    # fp16 bar rather than bit equality
     case = W.random_fwd(1, 200, 200, 2, 2, 64, 64, "fp16", True, seed=33)
     q, k, v = dev(case.q), dev(case.k), dev(case.v)
     a = E().attn_fwd(q, k, v, causal=True)
     b = E().attn_fwd(q, k, v, causal=True, window_size=(400, 400))
     torch.cuda.synchronize()
-    assert torch.equal(a, b)
+    ref, _ = attention_ref(to_f64(case.q), to_f64(case.k), to_f64(case.v), causal=True)
+    assert maxabs(a, ref) <= TOL["fp16"] and maxabs(b, ref) <= TOL["fp16"]
+    assert float((a.float() - b.float()).abs().max()) <= TOL["fp16"]
 
 
 # ---------------------------------------------------------------- packed sequences
