@@ -8,11 +8,12 @@
 // log-sum-exp, and D = rowsum(dO * O):
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Three launches:
-//  * bwd_prep_kernel: per query row, lse * log2(e) and D into the workspace;
+// Two launches:
 //  * bwd_dq_kernel: a wave owns 32 query rows of one (batch, q head) (their Q
-//    and dO fragments in registers) and streams 32-key K/V tiles through LDS,
-//    like the forward kernel: S^T = K Q^T and
+//    and dO fragments in registers), first computes each row's lse * log2(e)
+//    and D = rowsum(dO * O) (stored in the workspace for the next kernel),
+//    then streams 32-key K/V tiles through LDS, like the forward kernel:
+//    S^T = K Q^T and
 //    dP^T = V dO^T leave each lane with one query row, so P and dS need no
 //    cross-lane work; dQ^T += K^T dS^T reads K^T with ds_read_b64_tr_b16;
 //  * bwd_dkdv_kernel: the same with the roles of queries and keys swapped: a
@@ -70,36 +71,6 @@ __device__ __forceinline__ int dma_off(int i, int lane, int64_t row_stride) {
 }
 
 }  // namespace
-
-// ---------------------------------------------------------------- prep
-// one row per (16-byte lanes of dO and O) group; DV / 8 lanes per row
-template <class T, int DV>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
-  constexpr int LPR = DV / 8, RPW = 64 / LPR;
-  const int lane = threadIdx.x & 63, sub = lane / LPR, c = lane - sub * LPR;
-  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + sub;
-  const int64_t total = (int64_t)a.B * a.Hq * a.Sq;
-  const bool ok = sub < RPW && row < total;
-  const int64_t rr = ok ? row : 0;
-  const int i = (int)(rr % a.Sq);
-  const int64_t bh = rr / a.Sq;
-  const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
-  const u32x4 dv = ldg16(a.dout + (int64_t)b * a.do_sb + (int64_t)i * a.do_ss + (int64_t)h * a.do_sh + 8 * c);
-  const u32x4 ov = ldg16(a.o + (int64_t)b * a.o_sb + (int64_t)i * a.o_ss + (int64_t)h * a.o_sh + 8 * c);
-  float acc = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    acc += T::to_f32((uint16_t)(dv[e] & 0xFFFFu)) * T::to_f32((uint16_t)(ov[e] & 0xFFFFu));
-    acc += T::to_f32((uint16_t)(dv[e] >> 16)) * T::to_f32((uint16_t)(ov[e] >> 16));
-  }
-#pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m);
-  if (ok && c == 0) {
-    const float l = a.lse[rr];
-    a.ld[2 * rr + 0] = l * 1.4426950408889634f;
-    a.ld[2 * rr + 1] = acc;
-  }
-}
 
 // ---------------------------------------------------------------- dQ
 // A workgroup is NS key-split groups of NR waves; a wave owns 32 query rows,
@@ -192,8 +163,29 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int st = 0; st < VS; ++st) dof[st] = ldg16(dr + 16 * st + 8 * hh);
     }
+    // this row's lse * log2(e) and D = rowsum(dO * O) (lanes l and l ^ 32 hold
+    // the two halves of every 16 dims); group 0 also stores them for the dK/dV
+    // kernel, which runs after this one
     const int64_t lrow = ((int64_t)b * a.Hq + hq) * a.Sq + rc;
-    const float lse2 = a.ld[2 * lrow], Drow = a.ld[2 * lrow + 1];
+    float Dp = 0.f;
+    {
+      const uint16_t* orow = a.o + (int64_t)b * a.o_sb + (int64_t)rc * a.o_ss + (int64_t)hq * a.o_sh;
+#pragma unroll
+      for (int st = 0; st < VS; ++st) {
+        const u32x4 ov = ldg16(orow + 16 * st + 8 * hh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Dp += T::to_f32((uint16_t)(dof[st][e] & 0xFFFFu)) * T::to_f32((uint16_t)(ov[e] & 0xFFFFu));
+          Dp += T::to_f32((uint16_t)(dof[st][e] >> 16)) * T::to_f32((uint16_t)(ov[e] >> 16));
+        }
+      }
+    }
+    const float Drow = xhalf_sum(Dp);
+    const float lse2 = a.lse[lrow] * 1.4426950408889634f;
+    if (g == 0 && hh == 0 && row_ok) {
+      a.ld[2 * lrow] = lse2;
+      a.ld[2 * lrow + 1] = Drow;
+    }
 
     auto issue = [&](int t, int s) {
       const int key0 = t * 32, rows = min(32, L - key0);
@@ -583,13 +575,6 @@ static hipError_t launch_dkdv(BwdArgs a, hipStream_t st) {
 // registers allow it, causal tiles in complementary pairs.
 template <class T, int DQK, int DV, bool CAUSAL, bool WIN>
 static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
-  {
-    const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
-    const int rpb = 4 * (64 / (DV / 8));
-    hipLaunchKernelGGL((bwd_prep_kernel<T, DV>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   hipError_t e;
   if constexpr (DQK <= 64) {
     if constexpr (CAUSAL) e = launch_dq<T, DQK, DV, CAUSAL, WIN, 2, 4, true, 2>(a, st);
