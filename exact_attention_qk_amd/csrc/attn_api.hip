@@ -95,6 +95,7 @@ struct KVPlan {
   bool rotary = false;
   bool decode = false;      // split-KV path (few query rows per kv head)
   bool fused = false;       // decode kernel also appends the new rows and applies the rotary embedding
+  bool rotq = false;        // tiled kernel rotates q as it loads it (the append pass then skips q)
   int split_len = 0, num_splits = 0;
   size_t off_qrot = 0, off_o = 0, off_ml = 0, total = 0;
 };
@@ -109,8 +110,10 @@ KVPlan plan_kvcache(const attn_kvcache_params* p) {
   k.decode = R <= 16;
   k.fused = k.decode && (!k.rotary || (p->rotary_dim % 16 == 0 && aligned16(p->rotary_cos) &&
                                        aligned16(p->rotary_sin)));
+  k.rotq = !k.decode && k.rotary && p->rotary_dim % 16 == 0 && aligned16(p->rotary_cos) &&
+           aligned16(p->rotary_sin);
   size_t off = 0;
-  if (k.rotary && !k.fused) {
+  if (k.rotary && !k.fused && !k.rotq) {
     k.off_qrot = off;
     off = align_up(off + (size_t)p->B * p->Sq * p->Hq * p->Dqk * 2);
   }
@@ -566,7 +569,8 @@ int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream) {
   }
 
   char* ws = static_cast<char*>(p->workspace);
-  uint16_t* qrot = (plan.rotary && !plan.fused) ? reinterpret_cast<uint16_t*>(ws + plan.off_qrot) : nullptr;
+  uint16_t* qrot = (plan.rotary && !plan.fused && !plan.rotq) ? reinterpret_cast<uint16_t*>(ws + plan.off_qrot)
+                                                               : nullptr;
   const int64_t qr_sh = p->Dqk, qr_ss = (int64_t)p->Hq * p->Dqk, qr_sb = (int64_t)p->Sq * qr_ss;
 
   // 1. append new rows (rotating keys) and rotate the queries, unless the
@@ -600,7 +604,7 @@ int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream) {
       rowset(p->v_new, static_cast<uint16_t*>(p->v_cache.data), p->v_cache.stride_b, p->v_cache.stride_s,
              p->v_cache.stride_h, p->Snew, p->Hkv, p->Dv, false, true);
     }
-    if (plan.rotary) rowset(p->q, qrot, qr_sb, qr_ss, qr_sh, p->Sq, p->Hq, p->Dqk, true, false);
+    if (plan.rotary && !plan.rotq) rowset(p->q, qrot, qr_sb, qr_ss, qr_sh, p->Sq, p->Hq, p->Dqk, true, false);
   }
   if (ns > 0) {
     hipError_t he = attn::run_rope_rows(sets, ns, bf16, st);
@@ -648,6 +652,13 @@ int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream) {
     }
     he = attn::run_decode_attn(a, bf16, p->Dqk, p->Dv, p->causal != 0, st);
   } else {
+    if (plan.rotq) {
+      a.rotq = 1;
+      a.rcos = static_cast<const uint16_t*>(p->rotary_cos);
+      a.rsin = static_cast<const uint16_t*>(p->rotary_sin);
+      a.rd = p->rotary_dim;
+      a.rinter = p->rotary_interleaved ? 1 : 0;
+    }
     he = attn::run_tile_attn(a, bf16, p->Dqk, p->Dv, p->causal != 0, st);
   }
   if (he != hipSuccess) return hip_fail(he, "kvcache attention launch");

@@ -38,6 +38,7 @@ struct AttnArgs {
   const uint16_t* vn; int64_t vn_sb, vn_ss, vn_sh;
   const uint16_t* rcos; const uint16_t* rsin;   // [*, rd/2] tables, rows 16-byte aligned
   int rd, rinter;             // rotary width (0: none, else a multiple of 16), interleaved pairs
+  int rotq;                   // tiled kernel: rotate q as it is loaded (rd, rcos, rsin, rinter above)
 };
 
 // Gradients of attention (dQ, dK, dV) for a given dO.

@@ -77,7 +77,7 @@ __device__ __forceinline__ float dot2_sum<BF16>(uint32_t p, float acc) {
 // F8: q and k hold e4m3 codes (1 byte per element, strides in bytes) and S^T
 // runs on the 32x32x64 fp8 MFMA; V, P and the output stay 16-bit (T).
 template <class T, int DQK, int DV, bool CAUSAL, bool WIN, int RB, int NR, int NS, int BN, bool PAIR,
-          bool FASTC, int MINW, bool F8>
+          bool FASTC, int MINW, bool F8, bool ROTQ>
 __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs a) {
   constexpr int NKB = BN / 32;                           // 32-key MFMA blocks per tile
   constexpr int RW = 32 * RB;
@@ -240,6 +240,11 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
         q8[rb][s] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       }
+    } else if constexpr (ROTQ) {   // rotary embedding at the query's absolute position, as rope_apply rounds it
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+        qf[rb][s] = rope_chunk<T>(qbase + (int64_t)qr * a.q_ss, 16 * s + 8 * hh, a.rcos, a.rsin, (int64_t)off + qr,
+                                  a.rd, a.rinter != 0, false);
     } else {
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) qf[rb][s] = ldg16(qbase + (int64_t)qr * a.q_ss + 16 * s + 8 * hh);
@@ -508,7 +513,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
 
 // ---------------------------------------------------------------- launchers
 template <class T, int DQK, int DV, bool CAUSAL, bool WIN, int RB, int NR, int NS, int BN, bool PAIR, int MINW,
-          bool F8>
+          bool F8, bool ROTQ>
 static hipError_t launch_cfg(const AttnArgs& a0, bool fastc, hipStream_t st) {
   AttnArgs a = a0;
   constexpr int BM = NR * 32 * RB;
@@ -518,21 +523,21 @@ static hipError_t launch_cfg(const AttnArgs& a0, bool fastc, hipStream_t st) {
   a.xcd_remap = (units % 8 == 0) ? 1 : 0;
   const dim3 grid((unsigned)units), block(64 * NR * NS);
   if (fastc)
-    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, WIN, RB, NR, NS, BN, PAIR, true, MINW, F8>), grid,
+    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, WIN, RB, NR, NS, BN, PAIR, true, MINW, F8, ROTQ>), grid,
                        block, 0, st, a);
   else
-    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, WIN, RB, NR, NS, BN, PAIR, false, MINW, F8>), grid,
+    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, WIN, RB, NR, NS, BN, PAIR, false, MINW, F8, ROTQ>), grid,
                        block, 0, st, a);
   return hipGetLastError();
 }
 
 // Rows per workgroup and key splits per head dimension: small problems get
 // key-split groups so that every CU runs several waves.
-template <class T, int DQK, int DV, bool CAUSAL, bool WIN, bool F8 = false>
+template <class T, int DQK, int DV, bool CAUSAL, bool WIN, bool F8 = false, bool ROTQ = false>
 static hipError_t launch_dims(const AttnArgs& a, bool fastc, hipStream_t st) {
   const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
   if constexpr (DQK <= 16) {
-    return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 1, 64, false, 2, F8>(a, fastc, st);
+    return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 1, 64, false, 2, F8, ROTQ>(a, fastc, st);
   } else if constexpr (DQK <= 64) {
     // causal, no window, at most 65536 rows: complementary tile pairs (every
     // workgroup the same work); a causal band (window) gives every tile about
@@ -543,45 +548,48 @@ static hipError_t launch_dims(const AttnArgs& a, bool fastc, hipStream_t st) {
     // meet tiles past a shorter sequence's end: heavy-first order instead
     // (7 packed sequences: 21.3 -> 19.6 us)
     if (CAUSAL && !WIN && rows <= 256 * 256 && a.varlen)
-      return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 2, 4, 32, false, 2, F8>(a, fastc, st);
+      return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 2, 4, 32, false, 2, F8, ROTQ>(a, fastc, st);
     if (CAUSAL && !WIN && rows <= 256 * 256)
-      return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 2, 4, 32, true, 2, F8>(a, fastc, st);
-    return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 2, 64, false, 2, F8>(a, fastc, st);
+      return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 2, 4, 32, true, 2, F8, ROTQ>(a, fastc, st);
+    return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 2, 64, false, 2, F8, ROTQ>(a, fastc, st);
   } else {
     // one query block per wave keeps two waves per SIMD at these head sizes;
     // small head-128 problems also split the keys in two, so that a launch of
     // a few hundred workgroups still has two waves per SIMD (measured: D=128
     // B2 H8 S2048 49.8 -> 42.3 us, chunked prefill 66.4 -> 58.4 us)
     if (DQK <= 128 && rows <= 256 * 256)
-      return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 2, 64, false, 2, F8>(a, fastc, st);
-    return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 1, 64, false, 2, F8>(a, fastc, st);
+      return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 2, 64, false, 2, F8, ROTQ>(a, fastc, st);
+    return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 1, 64, false, 2, F8, ROTQ>(a, fastc, st);
   }
 }
 
-template <class T, int DQK, int DV, bool F8 = false>
+template <class T, int DQK, int DV, bool F8 = false, bool ROTQ = false>
 static hipError_t launch_tile_c(const AttnArgs& a, bool causal, bool fastc, hipStream_t st) {
   const bool win = a.wl < kNoWindow || a.wr < kNoWindow;
   if (win)
-    return causal ? launch_dims<T, DQK, DV, true, true, F8>(a, fastc, st)
-                  : launch_dims<T, DQK, DV, false, true, F8>(a, fastc, st);
-  return causal ? launch_dims<T, DQK, DV, true, false, F8>(a, fastc, st)
-                : launch_dims<T, DQK, DV, false, false, F8>(a, fastc, st);
+    return causal ? launch_dims<T, DQK, DV, true, true, F8, ROTQ>(a, fastc, st)
+                  : launch_dims<T, DQK, DV, false, true, F8, ROTQ>(a, fastc, st);
+  return causal ? launch_dims<T, DQK, DV, true, false, F8, ROTQ>(a, fastc, st)
+                : launch_dims<T, DQK, DV, false, false, F8, ROTQ>(a, fastc, st);
 }
 
-template <class T>
+template <class T, bool ROTQ>
 static hipError_t launch_tile_t(const AttnArgs& a, int dqk, int dv, bool causal, bool fastc, hipStream_t st) {
-  if (dqk == 16 && dv == 16) return launch_tile_c<T, 16, 16>(a, causal, fastc, st);
-  if (dqk == 64 && dv == 64) return launch_tile_c<T, 64, 64>(a, causal, fastc, st);
-  if (dqk == 128 && dv == 128) return launch_tile_c<T, 128, 128>(a, causal, fastc, st);
-  if (dqk == 192 && dv == 128) return launch_tile_c<T, 192, 128>(a, causal, fastc, st);
+  if (dqk == 16 && dv == 16) return launch_tile_c<T, 16, 16, false, ROTQ>(a, causal, fastc, st);
+  if (dqk == 64 && dv == 64) return launch_tile_c<T, 64, 64, false, ROTQ>(a, causal, fastc, st);
+  if (dqk == 128 && dv == 128) return launch_tile_c<T, 128, 128, false, ROTQ>(a, causal, fastc, st);
+  if (dqk == 192 && dv == 128) return launch_tile_c<T, 192, 128, false, ROTQ>(a, causal, fastc, st);
   return hipErrorInvalidValue;
 }
 
 hipError_t run_tile_attn(const AttnArgs& a, int dtype_bf16, int dqk, int dv, bool causal,
                          hipStream_t st) {
   const bool fastc = a.c > 0.f;
-  return dtype_bf16 ? launch_tile_t<BF16>(a, dqk, dv, causal, fastc, st)
-                    : launch_tile_t<F16>(a, dqk, dv, causal, fastc, st);
+  if (a.rotq)
+    return dtype_bf16 ? launch_tile_t<BF16, true>(a, dqk, dv, causal, fastc, st)
+                      : launch_tile_t<F16, true>(a, dqk, dv, causal, fastc, st);
+  return dtype_bf16 ? launch_tile_t<BF16, false>(a, dqk, dv, causal, fastc, st)
+                    : launch_tile_t<F16, false>(a, dqk, dv, causal, fastc, st);
 }
 
 hipError_t run_tile_attn_fp8(const AttnArgs& a, int d, bool causal, hipStream_t st) {

@@ -245,8 +245,11 @@ def test_kvcache_workspace_plan():
     q_rot = 8 * 1 * 32 * 128 * 2
     assert E.kvcache_workspace_size(p) == cnt + _al(q_rot) + _al(8 * 8 * nsp * R * 128 * 4) + \
         _al(8 * 8 * nsp * R * 2 * 4)
-    # chunked prefill (many query rows): only the rotated q copy
+    # chunked prefill (many query rows): q is rotated as the tiled kernel loads
+    # it when the rotary width is a multiple of 16; otherwise a rotated copy
     p, keep = _kv(B=4, Sq=512, Hq=16, Hkv=16, D=128, cap=4096, snew=512, rotary=64)
+    assert E.kvcache_workspace_size(p) == 0
+    p, keep = _kv(B=4, Sq=512, Hq=16, Hkv=16, D=128, cap=4096, snew=512, rotary=40)
     assert E.kvcache_workspace_size(p) == 4 * 512 * 16 * 128 * 2
     p, keep = _kv(B=4, Sq=512, Hq=16, Hkv=16, D=128, cap=4096, snew=512)
     assert E.kvcache_workspace_size(p) == 0
