@@ -332,6 +332,41 @@ def test_kvcache_fused_rope_equals_unfused():
     assert torch.equal(out_f, out_u)
 
 
+@pytest.mark.parametrize("snew,rot", [(1, 128), (64, 64), (64, 0)])
+def test_kvcache_fills_cache_exactly(snew, rot):
+    # c_b + Snew == capacity: the appended rows are the last rows of the cache,
+    # the rotary tables' last row is used, and nothing past the cache is touched
+    cap = 320
+    case = W.random_kvcache(3, snew, 8, 2, 128, 128, cap, "bf16", snew=snew, seqlens=[cap - snew, 0, 17],
+                            rotary_dim=rot, interleaved=snew > 1, seed=47 + snew)
+    _kv_check(case)
+    _kv_check(case, num_splits=4)
+
+
+def test_attn_check_rejects_lengths_that_do_not_fit(monkeypatch):
+    # ATTN_CHECK=1: the call copies the device-side lengths to the host and
+    # refuses them before anything is launched, so the caches stay untouched
+    monkeypatch.setenv("ATTN_CHECK", "1")
+    case = W.random_kvcache(2, 1, 4, 2, 64, 64, 64, "fp16", snew=1, seqlens=[10, 64], seed=49)
+    kc, vc = dev(case.k_cache), dev(case.v_cache)
+    with pytest.raises(E().AttnError) as ei:
+        E().attn_fwd_kvcache(dev(case.q), kc, vc, dev(case.k_new), dev(case.v_new),
+                             cache_seqlens=dev(case.cache_seqlens), causal=True)
+    torch.cuda.synchronize()
+    assert ei.value.code == -6
+    assert torch.equal(kc.cpu(), case.k_cache) and torch.equal(vc.cpu(), case.v_cache)
+    # lengths that fit pass the same check and give the oracle's result
+    _kv_check(W.random_kvcache(2, 1, 4, 2, 64, 64, 64, "fp16", snew=1, seqlens=[10, 63], seed=49))
+    # packed sequences: offsets that do not end at the packed row count are refused
+    vc_case = W.random_varlen([5, 7], [5, 7], 2, 2, 64, 64, "fp16", False, seed=51)
+    bad = vc_case.cu_seqlens_q.clone()
+    bad[-1] = bad[-1] - 1
+    with pytest.raises(E().AttnError) as ei:
+        E().attn_fwd_varlen(dev(vc_case.q), dev(vc_case.k), dev(vc_case.v), dev(bad), dev(vc_case.cu_seqlens_k),
+                            vc_case.max_seqlen_q)
+    assert ei.value.code == -2
+
+
 # ---------------------------------------------------------------- local window
 
 WINDOWS = [(0, 0), (16, 0), (37, 5), (-1, 20), (100, -1), (3, 70)]
