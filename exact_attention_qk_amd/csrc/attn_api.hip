@@ -45,6 +45,10 @@ int check_dtype(attn_dtype d) {
   return ATTN_OK;
 }
 
+// Key/value tiles of up to 64 rows are addressed with 32-bit byte offsets
+// (buffer resources and LDS-DMA offsets): 64 rows * 2 bytes * stride < 2^31.
+constexpr int64_t kMaxRowStride = (int64_t)1 << 24;
+
 int check_tensor(const attn_tensor4& t, const char* name) {
   if (!t.data) return fail(ATTN_E_NULL, "%s: data pointer is NULL", name);
   if (reinterpret_cast<uintptr_t>(t.data) % 16)
@@ -54,6 +58,9 @@ int check_tensor(const attn_tensor4& t, const char* name) {
                 (long long)t.stride_b, (long long)t.stride_s, (long long)t.stride_h);
   if (t.stride_b < 0 || t.stride_s < 0 || t.stride_h < 0)
     return fail(ATTN_E_SHAPE, "%s: negative stride", name);
+  if (t.stride_s >= kMaxRowStride)
+    return fail(ATTN_E_UNSUPPORTED, "%s: sequence stride %lld is not below 2^24 elements", name,
+                (long long)t.stride_s);
   return ATTN_OK;
 }
 
@@ -348,6 +355,9 @@ int check_fp8_tensor(const attn_tensor4& t, const char* name) {
                 (long long)t.stride_b, (long long)t.stride_s, (long long)t.stride_h);
   if (t.stride_b < 0 || t.stride_s < 0 || t.stride_h < 0)
     return fail(ATTN_E_SHAPE, "%s: negative stride", name);
+  if (t.stride_s >= kMaxRowStride)
+    return fail(ATTN_E_UNSUPPORTED, "%s: sequence stride %lld is not below 2^24 elements", name,
+                (long long)t.stride_s);
   return ATTN_OK;
 }
 

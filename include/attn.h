@@ -38,7 +38,9 @@
  *   [batch, seqlen, heads, head_dim] tensor; head_dim is contiguous (stride 1).
  *   Strided views (e.g. the .transpose(1, 2) views of issue #1402) are fine.
  *   Every data pointer must be 16-byte aligned and every stride a multiple of
- *   8 elements (16 bytes), so rows can be moved with 16-byte accesses.
+ *   8 elements (16 bytes), so rows can be moved with 16-byte accesses.  The
+ *   sequence stride must be below 2^24 elements (tiles of up to 64 rows are
+ *   addressed with 32-bit byte offsets); a larger one is ATTN_E_UNSUPPORTED.
  * - Ownership: the caller owns every buffer.  The library allocates no device
  *   or host memory on any call; the KV-cache path uses a caller-provided
  *   workspace sized by attn_fwd_kvcache_workspace_size().

@@ -76,6 +76,13 @@ def test_validate_fwd_ok_and_errors():
     p, keep = _fwd()
     p.v.stride_s = 100
     assert _code_fwd(p) == -4
+    # key tiles use 32-bit byte offsets: the sequence stride stays below 2^24 elements
+    p, keep = _fwd()
+    p.k.stride_s = 1 << 24
+    assert _code_fwd(p) == -3
+    assert b"2^24" in E.lib().attn_last_error()
+    p.k.stride_s = (1 << 24) - 8
+    assert _code_fwd(p) == 0
     p, keep = _fwd()
     p.dtype = 7
     assert _code_fwd(p) == -3
