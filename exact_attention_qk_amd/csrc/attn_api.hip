@@ -9,7 +9,6 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <string>
 #include <vector>
 
 #include "attn.h"
@@ -17,20 +16,19 @@
 
 namespace {
 
-thread_local std::string g_err;
+// The last failure's message, per thread, in a fixed buffer (no allocation).
+thread_local char g_err[512];
 
 int fail(int code, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
   va_end(ap);
-  g_err = buf;
   return code;
 }
 
 int ok() {
-  g_err.clear();
+  g_err[0] = '\0';
   return ATTN_OK;
 }
 
@@ -401,7 +399,7 @@ extern "C" {
 
 int attn_abi_version(void) { return 3; }
 
-const char* attn_last_error(void) { return g_err.c_str(); }
+const char* attn_last_error(void) { return g_err; }
 
 int attn_validate_fwd(const attn_fwd_params* p) { return validate_fwd(p); }
 int attn_validate_kvcache(const attn_kvcache_params* p) { return validate_kvcache(p); }

@@ -42,8 +42,9 @@
  *   sequence stride must be below 2^24 elements (tiles of up to 64 rows are
  *   addressed with 32-bit byte offsets); a larger one is ATTN_E_UNSUPPORTED.
  * - Ownership: the caller owns every buffer.  The library allocates no device
- *   or host memory on any call; the KV-cache path uses a caller-provided
- *   workspace sized by attn_fwd_kvcache_workspace_size().
+ *   or host memory on any call (the ATTN_CHECK=1 debug mode aside, which
+ *   copies lengths to host vectors); the KV-cache, backward and FP8 paths use
+ *   a caller-provided workspace sized by the matching *_workspace_size().
  * - Read-only inputs (q, k, v, k_new, v_new, cos/sin, cache_seqlens) may alias
  *   one another (issue #1402 passes one tensor as q, k and v).  out, lse, the
  *   caches and the workspace must not alias any other argument.
