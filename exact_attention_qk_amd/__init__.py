@@ -150,12 +150,28 @@ def _check(code):
         raise AttnError(code, _lib.attn_last_error().decode())
 
 
+def _on_gpu(*tensors):
+    """Every tensor a call hands to the kernels must be a GPU tensor, all on one device
+    (a host pointer reaching a kernel would be a memory fault, not an error code)."""
+    dev = None
+    for t in tensors:
+        if t is None or not isinstance(t, torch.Tensor):
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU, got one on %s" % t.device)
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors on different devices: %s and %s" % (dev, t.device))
+
+
 def _t4(t):
     if t is None:
         return Tensor4(None, 0, 0, 0)
-    assert t.dim() == 4, "expected a [batch, seqlen, heads, head_dim] tensor"
-    if t.shape[-1] > 1:
-        assert t.stride(-1) == 1, "head_dim must be contiguous"
+    if t.dim() != 4:
+        raise ValueError("expected a [batch, seqlen, heads, head_dim] tensor, got %d dims" % t.dim())
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError("head_dim must be contiguous (stride 1)")
     return Tensor4(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
 
 
@@ -195,6 +211,7 @@ def attn_fwd(q, k, v, causal=False, softmax_scale=None, out=None, return_lse=Fal
         out = torch.empty((B, Sq, Hq, Dv), dtype=q.dtype, device=q.device)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
     p = fwd_params(q, k, v, out, causal, softmax_scale, lse, window_size)
+    _on_gpu(q, k, v, out)
     _check(_lib.attn_fwd(ctypes.byref(p), _stream(q)))
     return (out, lse) if return_lse else out
 
@@ -205,7 +222,8 @@ def bwd_params(q, k, v, out, dout, lse, dq, dk, dv, causal=False, softmax_scale=
                window_size=(-1, -1)):
     B, Sq, Hq, Dqk = q.shape
     Sk, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
-    assert lse.dtype == torch.float32 and lse.is_contiguous() and tuple(lse.shape) == (B, Hq, Sq)
+    if not (lse.dtype == torch.float32 and lse.is_contiguous() and tuple(lse.shape) == (B, Hq, Sq)):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Sq] tensor from the forward call")
     return BwdParams(_dtype(q), B, Sq, Sk, Hq, Hkv, Dqk, Dv, _t4(q), _t4(k), _t4(v), _t4(out), _t4(dout),
                      _t4(dq), _t4(dk), _t4(dv), lse.data_ptr(), int(bool(causal)), _scale(softmax_scale),
                      int(window_size[0]), int(window_size[1]), None, 0)
@@ -228,6 +246,7 @@ def attn_bwd(dout, q, k, v, out, lse, causal=False, softmax_scale=None, window_s
     dk = torch.empty(k.shape, dtype=k.dtype, device=k.device) if dk is None else dk
     dv = torch.empty(v.shape, dtype=v.dtype, device=v.device) if dv is None else dv
     p = bwd_params(q, k, v, out, dout, lse, dq, dk, dv, causal, softmax_scale, window_size)
+    _on_gpu(dout, q, k, v, out, lse, dq, dk, dv)
     ws = _bwd_workspace(p, q.device)
     _check(_lib.attn_bwd(ctypes.byref(p), _stream(q)))
     del ws
@@ -237,6 +256,7 @@ def attn_bwd(dout, q, k, v, out, lse, causal=False, softmax_scale=None, window_s
 def prepare_bwd(dout, q, k, v, out, lse, dq, dk, dv, causal=False, softmax_scale=None,
                 window_size=(-1, -1)):
     p = bwd_params(q, k, v, out, dout, lse, dq, dk, dv, causal, softmax_scale, window_size)
+    _on_gpu(dout, q, k, v, out, lse, dq, dk, dv)
     ws = _bwd_workspace(p, q.device)
     return PreparedCall(_lib.attn_bwd, p, _stream(q), (dout, q, k, v, out, lse, dq, dk, dv, ws))
 
@@ -281,6 +301,7 @@ def attn_fwd_fp8(q, k, v, causal=False, softmax_scale=None, out=None, return_lse
         out = torch.empty((B, Sq, Hq, D), dtype=torch.bfloat16, device=q.device)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
     p = fp8_params(q, k, v, out, causal, softmax_scale, lse, window_size, descale_q, descale_k, descale_v)
+    _on_gpu(q, k, v, out)
     ws = _fp8_workspace(p, q.device)
     _check(_lib.attn_fwd_fp8(ctypes.byref(p), _stream(q)))
     del ws
@@ -290,6 +311,7 @@ def attn_fwd_fp8(q, k, v, causal=False, softmax_scale=None, out=None, return_lse
 def prepare_fp8(q, k, v, out, causal=False, softmax_scale=None, lse=None, window_size=(-1, -1),
                 descale_q=1.0, descale_k=1.0, descale_v=1.0):
     p = fp8_params(q, k, v, out, causal, softmax_scale, lse, window_size, descale_q, descale_k, descale_v)
+    _on_gpu(q, k, v, out, lse)
     ws = _fp8_workspace(p, q.device)
     return PreparedCall(_lib.attn_fwd_fp8, p, _stream(q), (q, k, v, out, lse, ws))
 
@@ -300,7 +322,8 @@ def _t3(x):
     """A packed [total, H, D] tensor as the ABI's tensor block (batch stride unused)."""
     if x is None:
         return Tensor4(None, 0, 0, 0)
-    assert x.dim() == 3 and x.stride(2) == 1
+    if x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("expected a packed [total, heads, head_dim] tensor with contiguous head_dim")
     return Tensor4(x.data_ptr(), 0, x.stride(0), x.stride(1))
 
 
@@ -309,7 +332,8 @@ def varlen_params(q, k, v, out, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal
     total_q, Hq, Dqk = q.shape
     total_k, Hkv, Dv = k.shape[0], k.shape[1], v.shape[2]
     for cu in (cu_seqlens_q, cu_seqlens_k):
-        assert cu.dtype == torch.int32 and cu.is_contiguous() and cu.is_cuda == q.is_cuda
+        if not (cu.dtype == torch.int32 and cu.is_contiguous() and cu.is_cuda == q.is_cuda):
+            raise ValueError("cu_seqlens must be contiguous int32 tensors on q's device")
     B = cu_seqlens_q.numel() - 1
     return VarlenParams(_dtype(q), B, total_q, total_k, int(max_seqlen_q), Hq, Hkv, Dqk, Dv,
                         _t3(q), _t3(k), _t3(v), _t3(out), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
@@ -328,6 +352,7 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal=Fa
     lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device) if return_lse else None
     p = varlen_params(q, k, v, out, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal, softmax_scale,
                       lse, window_size)
+    _on_gpu(q, k, v, out, cu_seqlens_q, cu_seqlens_k)
     _check(_lib.attn_fwd_varlen(ctypes.byref(p), _stream(q)))
     return (out, lse) if return_lse else out
 
@@ -336,6 +361,7 @@ def prepare_varlen(q, k, v, out, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causa
                    softmax_scale=None, lse=None, window_size=(-1, -1)):
     p = varlen_params(q, k, v, out, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal, softmax_scale,
                       lse, window_size)
+    _on_gpu(q, k, v, out, cu_seqlens_q, cu_seqlens_k, lse)
     return PreparedCall(_lib.attn_fwd_varlen, p, _stream(q),
                         (q, k, v, out, cu_seqlens_q, cu_seqlens_k, lse))
 
@@ -349,7 +375,8 @@ def kvcache_params(q, k_cache, v_cache, k=None, v=None, rotary_cos=None, rotary_
     cap, Hkv, Dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
     snew = 0 if k is None else k.shape[1]
     if isinstance(cache_seqlens, torch.Tensor):
-        assert cache_seqlens.dtype == torch.int32 and cache_seqlens.is_contiguous()
+        if not (cache_seqlens.dtype == torch.int32 and cache_seqlens.is_contiguous()):
+            raise ValueError("cache_seqlens must be an int or a contiguous int32 tensor")
         cs_scalar, cs_ptr = 0, cache_seqlens.data_ptr()
     else:
         cs_scalar, cs_ptr = int(cache_seqlens), None
@@ -390,6 +417,7 @@ def attn_fwd_kvcache(q, k_cache, v_cache, k=None, v=None, rotary_cos=None, rotar
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
     p = kvcache_params(q, k_cache, v_cache, k, v, rotary_cos, rotary_sin, cache_seqlens, causal,
                        softmax_scale, bool(rotary_interleaved), out, lse, None, num_splits, window_size)
+    _on_gpu(q, k_cache, v_cache, k, v, rotary_cos, rotary_sin, cache_seqlens, out, workspace)
     need = kvcache_workspace_size(p)
     if workspace is None or workspace.numel() < need + 256:
         workspace = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
@@ -406,6 +434,8 @@ def attn_fwd_kvcache(q, k_cache, v_cache, k=None, v=None, rotary_cos=None, rotar
 def rope_params(x, cos, sin, offsets=0, interleaved=False, conjugate=False, out=None):
     B, S, H, D = x.shape
     if isinstance(offsets, torch.Tensor):
+        if not (offsets.dtype == torch.int32 and offsets.is_contiguous()):
+            raise ValueError("offsets must be an int or a contiguous int32 tensor")
         off_s, off_p = 0, offsets.data_ptr()
     else:
         off_s, off_p = int(offsets), None
@@ -419,6 +449,7 @@ def rope_apply(x, cos, sin, offsets=0, interleaved=False, conjugate=False, out=N
     if out is None:
         out = x if inplace else torch.empty_like(x)
     p = rope_params(x, cos, sin, offsets, interleaved, conjugate, out)
+    _on_gpu(x, cos, sin, offsets, out)
     _check(_lib.rope_apply(ctypes.byref(p), _stream(x)))
     return out
 
@@ -444,6 +475,7 @@ class PreparedCall:
 
 def prepare_fwd(q, k, v, out, causal=False, softmax_scale=None, lse=None, window_size=(-1, -1)):
     p = fwd_params(q, k, v, out, causal, softmax_scale, lse, window_size)
+    _on_gpu(q, k, v, out, lse)
     return PreparedCall(_lib.attn_fwd, p, _stream(q), (q, k, v, out, lse))
 
 
@@ -452,6 +484,7 @@ def prepare_kvcache(q, k_cache, v_cache, k, v, out, *, rotary_cos=None, rotary_s
                     num_splits=0, lse=None, window_size=(-1, -1)):
     p = kvcache_params(q, k_cache, v_cache, k, v, rotary_cos, rotary_sin, cache_seqlens, causal,
                        softmax_scale, rotary_interleaved, out, lse, None, num_splits, window_size)
+    _on_gpu(q, k_cache, v_cache, k, v, out, rotary_cos, rotary_sin, cache_seqlens, lse)
     need = kvcache_workspace_size(p)
     ws = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
     off = (-ws.data_ptr()) % 256

@@ -167,6 +167,21 @@ def test_binding_rejects_other_dtypes_before_any_launch():
         E.attn_fwd(q, q, q)
 
 
+def test_binding_refuses_host_tensors_before_any_launch():
+    # a host pointer handed to a kernel would be a GPU memory fault: the binding refuses it
+    q = torch.zeros(1, 4, 1, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        E.attn_fwd(q, q, q)
+    kc = torch.zeros(1, 8, 1, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        E.attn_fwd_kvcache(q[:, :1], kc, kc, cache_seqlens=0)
+    cs = torch.zeros(8, 32, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        E.rope_apply(q, cs, cs)
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        E.attn_fwd_varlen(q[0], q[0], q[0], torch.zeros(2, dtype=torch.int64), torch.zeros(2, dtype=torch.int32), 4)
+
+
 def _kv(B=2, Sq=1, Hq=8, Hkv=2, D=128, cap=64, snew=1, seqlens=5, rotary=0, dtype=torch.bfloat16,
         **kw):
     q = _t((B, Sq, Hq, D), dtype)
