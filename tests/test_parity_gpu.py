@@ -650,3 +650,75 @@ def test_fp8_no_keys_gives_zero_rows():
 def test_workload_fwd_fp8_d64_full(causal):
     # the bench configuration: B=2, H=8, S=2048, D=64, every output row
     _fp8_check(W.fwd_fp8_d64(causal))
+
+
+# ---------------------------------------------------------------- streams and graphs
+
+def test_calls_follow_the_current_stream():
+    # work is enqueued on torch's current stream: on a side stream the result
+    # matches the default-stream call once that stream is synchronized
+    case = W.random_fwd(2, 300, 300, 4, 2, 64, 64, "fp16", True, seed=61)
+    q, k, v = dev(case.q), dev(case.k), dev(case.v)
+    ref = E().attn_fwd(q, k, v, causal=True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        out = E().attn_fwd(q, k, v, causal=True)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+def test_graph_capture_replays_match_eager():
+    # the calls enqueue kernels only (no allocation inside the library, no
+    # memset, no host synchronisation), so a HIP graph can hold them; every
+    # replay, with eager work between replays, must give the eager bits
+    mod = E()
+    fc = W.random_fwd(2, 300, 300, 4, 2, 64, 64, "fp16", True, seed=63)
+    q, k, v = dev(fc.q), dev(fc.k), dev(fc.v)
+    kc = W.random_kvcache(3, 1, 8, 2, 128, 128, 512, "bf16", snew=1, seqlens=[0, 200, 511 - 1],
+                          rotary_dim=128, seed=65)
+    kq, kn, vn = dev(kc.q), dev(kc.k_new), dev(kc.v_new)
+    kcache, vcache = dev(kc.k_cache), dev(kc.v_cache)
+    cs, cos, sin = dev(kc.cache_seqlens), dev(kc.rotary_cos), dev(kc.rotary_sin)
+    dout = torch.randn(q.shape, generator=torch.Generator().manual_seed(67)).to(q.dtype).to(DEV)
+
+    fout = torch.empty_like(q)
+    lse = torch.empty((2, 4, 300), dtype=torch.float32, device=DEV)
+    kout = torch.empty((3, 1, 8, 128), dtype=kq.dtype, device=DEV)
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device=DEV)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def run():
+        mod.attn_fwd(q, k, v, causal=True, out=fout, return_lse=False)
+        o2, l2 = mod.attn_fwd(q, k, v, causal=True, return_lse=True)
+        lse.copy_(l2)
+        mod.attn_fwd_kvcache(kq, kcache, vcache, kn, vn, rotary_cos=cos, rotary_sin=sin, cache_seqlens=cs,
+                             causal=True, rotary_interleaved=False, out=kout, workspace=ws)
+        mod.attn_bwd(dout, q, k, v, fout, lse, causal=True, dq=dq, dk=dk, dv=dv)
+
+    run()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (fout, lse, kout, kcache, vcache, dq, dk, dv)]
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()                                   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (fout, lse, kout, dq, dk, dv):
+            t.fill_(float("nan"))
+        mod.attn_fwd(q, k, v, causal=False)     # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (fout, lse, kout, kcache, vcache, dq, dk, dv)
+        for name, a, b in zip(("out", "lse", "kvcache out", "k_cache", "v_cache", "dq", "dk", "dv"), got, eager):
+            assert torch.equal(a, b), "replay %d: %s differs from the eager call" % (rep, name)
+
