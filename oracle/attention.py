@@ -6,7 +6,7 @@ accuracy check of Step 4): scores = Q K^T scaled by ``softmax_scale``,
 row softmax, weights times V.  The full score matrix of one (batch, head) is
 materialised; nothing is tiled, fused or reordered.
 
-Readings of points the pages leave open (listed again in the design doc):
+Readings of points the pages leave open:
 
 * default scale is 1/sqrt(head_dim of q and k) (Workflow 2 Step 2 passes
   ``softmax_scale=None`` for the automatic scale; Workflow 1 divides by

@@ -3,7 +3,7 @@
 The skill page "Flash Attention - Fast Memory-Efficient Attention", Workflow 3
 (H100 FP8 optimization with FlashAttention-3), converts q, k and v to FP8 and
 runs attention on them.  The page breaks off inside the conversion step, so
-the format and the scaling are readings (listed again in the design doc):
+the format and the scaling are readings:
 
 * the 8-bit format is e4m3 in its "fn" form: 1 sign bit, 4 exponent bits with
   bias 7, 3 mantissa bits, subnormals when the exponent field is 0, no

@@ -16,7 +16,7 @@ interleaved pairs 2j with 2j+1.  For pair (x1, x2) and table entries (c, s):
 ``conjugate`` rotates by the opposite angle (s -> -s).  Dimensions at or past
 ``rotary_dim`` pass through unchanged.
 
-Rounding contract (the pages are silent; the reading is stated in the design doc):
+Rounding contract (the pages are silent; this is the reading taken):
 inputs and tables are dtype values; each output is the exact value
 x1*c - x2*s (or x1*s + x2*c) rounded once to fp32, then rounded to the dtype
 (round-to-nearest-even both times).  The products of two 16-bit floats are
