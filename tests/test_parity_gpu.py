@@ -534,6 +534,31 @@ def test_bwd_gqa_group_of_eight():
     _bwd_check(case, seed=9)
 
 
+def test_bwd_strided_views():
+    # q, k, v, dO as transposed views of [B, H, S, D] memory; dq, dk, dv written
+    # into transposed views as well (only their own elements)
+    g = torch.Generator().manual_seed(71)
+    B, S, Hq, Hkv, D = 2, 150, 4, 2, 128
+    qm = torch.randn(B, Hq, S, D, generator=g).to(torch.bfloat16)
+    km = torch.randn(B, Hkv, S, D, generator=g).to(torch.bfloat16)
+    vm = torch.randn(B, Hkv, S, D, generator=g).to(torch.bfloat16)
+    dom = torch.randn(B, Hq, S, D, generator=g).to(torch.bfloat16)
+    q, k, v, do = (dev(t).transpose(1, 2) for t in (qm, km, vm, dom))
+    assert not q.is_contiguous()
+    out, lse = E().attn_fwd(q, k, v, causal=True, return_lse=True)
+    dq = torch.full((B, Hq, S, D), 7.0, dtype=torch.bfloat16, device=DEV).transpose(1, 2)
+    dk = torch.full((B, Hkv, S, D), 7.0, dtype=torch.bfloat16, device=DEV).transpose(1, 2)
+    dv = torch.full((B, Hkv, S, D), 7.0, dtype=torch.bfloat16, device=DEV).transpose(1, 2)
+    E().attn_bwd(do, q, k, v, out, lse, causal=True, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    rq, rk, rv = attention_bwd_ref(to_f64(qm.transpose(1, 2)), to_f64(km.transpose(1, 2)),
+                                   to_f64(vm.transpose(1, 2)), to_f64(dom.transpose(1, 2)), causal=True)
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        err = maxabs(got, ref)
+        bar = TOL["bf16"] * max(1.0, float(np.max(np.abs(ref))))
+        assert err <= bar, "%s max abs err %.3e > %.3e" % (name, err, bar)
+
+
 def test_bwd_no_keys_gives_zero_gradients():
     q = torch.randn(1, 5, 2, 64, device=DEV).half()
     k = torch.zeros(1, 0, 2, 64, device=DEV).half()
