@@ -279,6 +279,15 @@ def test_kvcache_decode_two_tokens_full_rows(causal):
     _kv_check(case)
 
 
+def test_kvcache_decode_many_splits():
+    # capacity 131072 with one kv head per batch: the plan makes 256-key
+    # splits, so the merge combines up to 512 splits per row (several passes
+    # of 64); the second batch is half full
+    case = W.random_kvcache(2, 1, 8, 1, 128, 128, 131072, "bf16", snew=1, seqlens=[131071, 70000],
+                            rotary_dim=128, seed=73)
+    _kv_check(case)
+
+
 def test_kvcache_scalar_and_tensor_seqlens_agree():
     a = W.random_kvcache(2, 1, 4, 1, 128, 128, 512, "bf16", snew=1, seqlens=[300, 300],
                          rotary_dim=128, seed=15)
