@@ -36,6 +36,8 @@
 //    blocks that cross a band edge;
 //  * epilogue: O / l rounded to the output type, staged through LDS so each
 //    lane stores 16 contiguous bytes of an output row.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "attn_args.hpp"
 #include "launchers.hpp"
@@ -271,8 +273,11 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
   const int tr_t = (lane & 15) >> 2;
   const int tr_q = lane & 3;
 
-  for (int it = 0; it < nit; ++it) {
-    const int s = it & 1;
+  // One key tile per call; the loop makes two calls per trip so that each
+  // call's LDS stage is a constant (its addresses become instruction offsets
+  // of loop-invariant registers).
+  auto iter = [&](const int it, auto SC) {
+    constexpr int s = decltype(SC)::value;   // LDS stage of this iteration
     const int tr = it * NS + g;                  // tile index inside the unit
     const int t = t_lo + tr;
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this lane's DMA for stage s landed
@@ -280,7 +285,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
     if (it + 1 < nit && tr + NS < ntiles) issue(t + NS, s ^ 1);
 
     const int key0 = t * BN;
-    if (tr >= ntiles || !wave_active || key0 >= wkend || (WIN && key0 + BN <= wkbeg)) continue;
+    if (tr >= ntiles || !wave_active || key0 >= wkend || (WIN && key0 + BN <= wkbeg)) return;
     const uint16_t* kt = lds16 + (g * 2 + s) * STAGE;
     const uint16_t* vt = kt + KT;
 
@@ -409,6 +414,10 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
         }
       }
     }
+  };
+  for (int it = 0; it < nit; it += 2) {
+    iter(it, std::integral_constant<int, 0>{});
+    if (it + 1 < nit) iter(it + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- merge the key-split groups (exact log-sum-exp combination)
