@@ -205,46 +205,52 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void bwd_dq_kernel(BwdArgs a) {
     for (int i = 0; i < QB; ++i) dq[i] = (f32x16){};
 
     if (g < ntiles) issue(t_lo + g, 0);
-    for (int it = 0; it < nit; ++it) {
-      const int s = it & 1;
-      const int tr = it * NS + g;                 // this group's tile, relative to t_lo
-      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this lane's part of the tile landed
-      __syncthreads();                      // ... every lane's; stage s^1 is free again
-      if (tr + NS < ntiles) issue(t_lo + tr + NS, s ^ 1);
-      const int key0 = (t_lo + tr) * 32;
-      if (tr >= ntiles || !wave_active || key0 >= wkend || (WIN && key0 + 32 <= wkbeg)) continue;
-      const uint16_t* kt = lds16 + (g * 2 + s) * STAGE;
-      const uint16_t* vt = kt + KT;
-      // S^T = K Q^T and dP^T = V dO^T, keys in the forward kernel's order
-      const int prow = perm32(lane & 31);
-      f32x16 sc = (f32x16){}, dp = (f32x16){};
+    // two tiles per trip, the inner loop unrolled: each copy's LDS stage s is a
+    // constant, so its LDS reads take immediate offsets
+    for (int it0 = 0; it0 < nit; it0 += 2) {
 #pragma unroll
-      for (int st = 0; st < KS; ++st) sc = T::mfma32(row_frag<DQK, true>(kt, prow, 2 * st + hh), qf[st], sc);
-#pragma unroll
-      for (int st = 0; st < VS; ++st) dp = T::mfma32(row_frag<DV, false>(vt, prow, 2 * st + hh), dof[st], dp);
-      u32x4 dsf[2];
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        float d[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * t2 + e;
-          const int key = key0 + 16 * t2 + 8 * hh + e;
-          bool ok = row_ok && key < L;
-          if (WIN || CAUSAL) ok = ok && key <= qpos + wrgt;
-          if (WIN) ok = ok && key >= qpos - wlft;
-          const float p = ok ? fast_exp2(__builtin_fmaf(sc[r], c, -lse2)) : 0.f;
-          d[e] = p * (dp[r] - Drow);
+      for (int s = 0; s < 2; ++s) {
+        const int it = it0 + s;
+        if (it >= nit) break;
+        const int tr = it * NS + g;                 // this group's tile, relative to t_lo
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this lane's part of the tile landed
+        __syncthreads();                      // ... every lane's; stage s^1 is free again
+        if (tr + NS < ntiles) issue(t_lo + tr + NS, s ^ 1);
+        const int key0 = (t_lo + tr) * 32;
+        if (tr >= ntiles || !wave_active || key0 >= wkend || (WIN && key0 + 32 <= wkbeg)) continue;
+        const uint16_t* kt = lds16 + (g * 2 + s) * STAGE;
+        const uint16_t* vt = kt + KT;
+        // S^T = K Q^T and dP^T = V dO^T, keys in the forward kernel's order
+        const int prow = perm32(lane & 31);
+        f32x16 sc = (f32x16){}, dp = (f32x16){};
+  #pragma unroll
+        for (int st = 0; st < KS; ++st) sc = T::mfma32(row_frag<DQK, true>(kt, prow, 2 * st + hh), qf[st], sc);
+  #pragma unroll
+        for (int st = 0; st < VS; ++st) dp = T::mfma32(row_frag<DV, false>(vt, prow, 2 * st + hh), dof[st], dp);
+        u32x4 dsf[2];
+  #pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          float d[8];
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * t2 + e;
+            const int key = key0 + 16 * t2 + 8 * hh + e;
+            bool ok = row_ok && key < L;
+            if (WIN || CAUSAL) ok = ok && key <= qpos + wrgt;
+            if (WIN) ok = ok && key >= qpos - wlft;
+            const float p = ok ? fast_exp2(__builtin_fmaf(sc[r], c, -lse2)) : 0.f;
+            d[e] = p * (dp[r] - Drow);
+          }
+          dsf[t2] = (u32x4){packw<T>(d[0], d[1]), packw<T>(d[2], d[3]), packw<T>(d[4], d[5]), packw<T>(d[6], d[7])};
         }
-        dsf[t2] = (u32x4){packw<T>(d[0], d[1]), packw<T>(d[2], d[3]), packw<T>(d[4], d[5]), packw<T>(d[6], d[7])};
-      }
-      // dQ^T += K^T dS^T
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const int rowa = 16 * t2 + 8 * hh + tr_t;
-#pragma unroll
-        for (int i = 0; i < QB; ++i)
-          dq[i] = T::mfma32(tr_frag<DQK, true>(kt, rowa, i * 32 + 16 * (grp & 1) + 4 * tr_q), dsf[t2], dq[i]);
+        // dQ^T += K^T dS^T
+  #pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const int rowa = 16 * t2 + 8 * hh + tr_t;
+  #pragma unroll
+          for (int i = 0; i < QB; ++i)
+            dq[i] = T::mfma32(tr_frag<DQK, true>(kt, rowa, i * 32 + 16 * (grp & 1) + 4 * tr_q), dsf[t2], dq[i]);
+        }
       }
     }
 
@@ -425,66 +431,72 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void bwd_dkdv_kernel(BwdArgs a)
     for (int i = 0; i < VB; ++i) dv[i] = (f32x16){};
 
     if (g < nsteps) issue(g, 0);
-    for (int it = 0; it < nit; ++it) {
-      const int s = it & 1;
-      const int n = it * NS + g;
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
-      if (n + NS < nsteps) issue(n + NS, s ^ 1);
-      if (n >= nsteps || wk0 >= L) continue;
-      const int r0 = (rb_lo + n % nrb) * 32;
-      // this wave's keys [wk0, wk0 + 32) against the block's band of rows
-      if ((WIN || CAUSAL) && wk0 > off + r0 + 31 + wrgt) continue;
-      if (WIN && wk0 + 31 < off + r0 - wlft) continue;
-      const uint16_t* qt = lds16 + RES + (g * 2 + s) * STAGE;
-      const uint16_t* ot = qt + QT;
-      const float* lt = reinterpret_cast<const float*>(ot + OT);
-      // S = Q K^T and dP = dO V^T: a lane owns a key; its registers cover rows
-      // r0 + 16 (r >> 3) + 8 hh + (r & 7)
-      const int prow = perm32(lane & 31);
-      f32x16 sc = (f32x16){}, dp = (f32x16){};
+    // two tiles per trip, the inner loop unrolled: each copy's LDS stage s is a
+    // constant, so its LDS reads take immediate offsets
+    for (int it0 = 0; it0 < nit; it0 += 2) {
 #pragma unroll
-      for (int st = 0; st < KS; ++st)
-        sc = T::mfma32(row_frag<DQK, true>(qt, prow, 2 * st + hh),
-                       KVL ? row_frag<DQK, true>(kres, lane & 31, 2 * st + hh) : kf[KVL ? 0 : st], sc);
-#pragma unroll
-      for (int st = 0; st < VS; ++st)
-        dp = T::mfma32(row_frag<DV, false>(ot, prow, 2 * st + hh),
-                       KVL ? row_frag<DV, true>(vres, lane & 31, 2 * st + hh) : vf[KVL ? 0 : st], dp);
-      u32x4 pf[2], dsf[2];
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lt + 2 * (16 * t2 + 8 * hh));
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lt + 2 * (16 * t2 + 8 * hh) + 4);
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(lt + 2 * (16 * t2 + 8 * hh) + 8);
-        const f32x4 l3 = *reinterpret_cast<const f32x4*>(lt + 2 * (16 * t2 + 8 * hh) + 12);
-        const float lsev[8] = {l0[0], l0[2], l1[0], l1[2], l2[0], l2[2], l3[0], l3[2]};
-        const float dv8[8] = {l0[1], l0[3], l1[1], l1[3], l2[1], l2[3], l3[1], l3[3]};
-        float p[8], d[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * t2 + e;
-          const int qrow = r0 + 16 * t2 + 8 * hh + e;
-          const int qpos = off + qrow;
-          bool ok = key_ok && qrow < a.Sq;
-          if (WIN || CAUSAL) ok = ok && key <= qpos + wrgt;
-          if (WIN) ok = ok && key >= qpos - wlft;
-          p[e] = ok ? fast_exp2(__builtin_fmaf(sc[r], c, -lsev[e])) : 0.f;
-          d[e] = p[e] * (dp[r] - dv8[e]);
+      for (int s = 0; s < 2; ++s) {
+        const int it = it0 + s;
+        if (it >= nit) break;
+        const int n = it * NS + g;
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        if (n + NS < nsteps) issue(n + NS, s ^ 1);
+        if (n >= nsteps || wk0 >= L) continue;
+        const int r0 = (rb_lo + n % nrb) * 32;
+        // this wave's keys [wk0, wk0 + 32) against the block's band of rows
+        if ((WIN || CAUSAL) && wk0 > off + r0 + 31 + wrgt) continue;
+        if (WIN && wk0 + 31 < off + r0 - wlft) continue;
+        const uint16_t* qt = lds16 + RES + (g * 2 + s) * STAGE;
+        const uint16_t* ot = qt + QT;
+        const float* lt = reinterpret_cast<const float*>(ot + OT);
+        // S = Q K^T and dP = dO V^T: a lane owns a key; its registers cover rows
+        // r0 + 16 (r >> 3) + 8 hh + (r & 7)
+        const int prow = perm32(lane & 31);
+        f32x16 sc = (f32x16){}, dp = (f32x16){};
+  #pragma unroll
+        for (int st = 0; st < KS; ++st)
+          sc = T::mfma32(row_frag<DQK, true>(qt, prow, 2 * st + hh),
+                         KVL ? row_frag<DQK, true>(kres, lane & 31, 2 * st + hh) : kf[KVL ? 0 : st], sc);
+  #pragma unroll
+        for (int st = 0; st < VS; ++st)
+          dp = T::mfma32(row_frag<DV, false>(ot, prow, 2 * st + hh),
+                         KVL ? row_frag<DV, true>(vres, lane & 31, 2 * st + hh) : vf[KVL ? 0 : st], dp);
+        u32x4 pf[2], dsf[2];
+  #pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const f32x4 l0 = *reinterpret_cast<const f32x4*>(lt + 2 * (16 * t2 + 8 * hh));
+          const f32x4 l1 = *reinterpret_cast<const f32x4*>(lt + 2 * (16 * t2 + 8 * hh) + 4);
+          const f32x4 l2 = *reinterpret_cast<const f32x4*>(lt + 2 * (16 * t2 + 8 * hh) + 8);
+          const f32x4 l3 = *reinterpret_cast<const f32x4*>(lt + 2 * (16 * t2 + 8 * hh) + 12);
+          const float lsev[8] = {l0[0], l0[2], l1[0], l1[2], l2[0], l2[2], l3[0], l3[2]};
+          const float dv8[8] = {l0[1], l0[3], l1[1], l1[3], l2[1], l2[3], l3[1], l3[3]};
+          float p[8], d[8];
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * t2 + e;
+            const int qrow = r0 + 16 * t2 + 8 * hh + e;
+            const int qpos = off + qrow;
+            bool ok = key_ok && qrow < a.Sq;
+            if (WIN || CAUSAL) ok = ok && key <= qpos + wrgt;
+            if (WIN) ok = ok && key >= qpos - wlft;
+            p[e] = ok ? fast_exp2(__builtin_fmaf(sc[r], c, -lsev[e])) : 0.f;
+            d[e] = p[e] * (dp[r] - dv8[e]);
+          }
+          pf[t2] = (u32x4){packw<T>(p[0], p[1]), packw<T>(p[2], p[3]), packw<T>(p[4], p[5]), packw<T>(p[6], p[7])};
+          dsf[t2] = (u32x4){packw<T>(d[0], d[1]), packw<T>(d[2], d[3]), packw<T>(d[4], d[5]), packw<T>(d[6], d[7])};
         }
-        pf[t2] = (u32x4){packw<T>(p[0], p[1]), packw<T>(p[2], p[3]), packw<T>(p[4], p[5]), packw<T>(p[6], p[7])};
-        dsf[t2] = (u32x4){packw<T>(d[0], d[1]), packw<T>(d[2], d[3]), packw<T>(d[4], d[5]), packw<T>(d[6], d[7])};
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const int rowa = 16 * t2 + 8 * hh + tr_t;
-#pragma unroll
-        for (int i = 0; i < VB; ++i)
-          dv[i] = T::mfma32(tr_frag<DV, false>(ot, rowa, i * 32 + 16 * (grp & 1) + 4 * tr_q), pf[t2], dv[i]);
-#pragma unroll
-        for (int i = 0; i < KB; ++i)
-          dk[i] = T::mfma32(tr_frag<DQK, true>(qt, rowa, i * 32 + 16 * (grp & 1) + 4 * tr_q), dsf[t2], dk[i]);
+        // dV^T += dO^T P and dK^T += Q^T dS
+  #pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const int rowa = 16 * t2 + 8 * hh + tr_t;
+  #pragma unroll
+          for (int i = 0; i < VB; ++i)
+            dv[i] = T::mfma32(tr_frag<DV, false>(ot, rowa, i * 32 + 16 * (grp & 1) + 4 * tr_q), pf[t2], dv[i]);
+  #pragma unroll
+          for (int i = 0; i < KB; ++i)
+            dk[i] = T::mfma32(tr_frag<DQK, true>(qt, rowa, i * 32 + 16 * (grp & 1) + 4 * tr_q), dsf[t2], dk[i]);
+        }
       }
     }
 
