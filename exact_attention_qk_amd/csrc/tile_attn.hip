@@ -31,10 +31,6 @@
 //    max exceeds it by more than 2^8, so the O rescale is rare and P stays
 //    below 256; the row sum is accumulated from the packed P with v_dot2, so
 //    numerator and denominator use the same rounded weights;
-//  * QS (head size 64, no mask band): c is folded into q at load (q * c
-//    rounded to the input type) and each S^T accumulator starts from -m, so
-//    the MFMA yields s*c - m directly and P = exp2 of it: 32 FMAs per tile
-//    fewer on the VALU, which bounds this loop;
 //  * causal and local windows: a unit walks only the key tiles its rows can
 //    see, waves skip 32-key blocks outside their rows' band and mask only
 //    blocks that cross a band edge;
@@ -82,9 +78,8 @@ __device__ __forceinline__ float dot2_sum<BF16>(uint32_t p, float acc) {
 
 // F8: q and k hold e4m3 codes (1 byte per element, strides in bytes) and S^T
 // runs on the 32x32x64 fp8 MFMA; V, P and the output stay 16-bit (T).
-// QS (requires FASTC, 16-bit q, 0 < c <= 1): q is multiplied by c at load.
 template <class T, int DQK, int DV, bool CAUSAL, bool WIN, int RB, int NR, int NS, int BN, bool PAIR,
-          bool FASTC, int MINW, bool F8, bool ROTQ, bool QS>
+          bool FASTC, int MINW, bool F8, bool ROTQ>
 __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs a) {
   constexpr int NKB = BN / 32;                           // 32-key MFMA blocks per tile
   constexpr int RW = 32 * RB;
@@ -258,32 +253,16 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
     }
   }
 
-  static_assert(!QS || (FASTC && !F8), "q scaling needs the positive-scale 16-bit path");
-  if constexpr (QS) {   // S^T then comes out in log2 units
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        u32x4 v = qf[rb][s];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          v[e] = T::pack2(T::to_f32((uint16_t)(v[e] & 0xFFFFu)) * a.c, T::to_f32((uint16_t)(v[e] >> 16)) * a.c);
-        qf[rb][s] = v;
-      }
-  }
-
   f32x16 o[RB][DVB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int i = 0; i < DVB; ++i) o[rb][i] = (f32x16){};
   float m_use[RB], l_run[RB];   // m_use in log2 units (score * c)
-  float m_acc[RB];               // QS: the S^T accumulators start from -m_acc
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m_use[rb] = -__builtin_inff();
     l_run[rb] = 0.f;
-    m_acc[rb] = 0.f;
   }
   const float c = FASTC ? a.c : 1.f;
   const float cpre = a.c;   // general path: scores are multiplied by c first
@@ -339,15 +318,8 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
           for (int st = 0; st < KSTEPS; ++st) {
             const u32x4 af = *reinterpret_cast<const u32x4*>(kr + (((2 * st + hh) ^ sw) << 3));
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-              f32x16 c0 = (f32x16){};
-              if constexpr (QS)
-                if (st == 0) {
-#pragma unroll
-                  for (int r = 0; r < 16; ++r) c0[r] = -m_acc[rb];
-                }
-              sc[rb][kb] = T::mfma32(af, qf[rb][st], st == 0 ? c0 : sc[rb][kb]);
-            }
+            for (int rb = 0; rb < RB; ++rb)
+              sc[rb][kb] = T::mfma32(af, qf[rb][st], st == 0 ? (f32x16){} : sc[rb][kb]);
           }
         }
       } else {
@@ -386,8 +358,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[rb][kb][r]);
-      if constexpr (QS) mx = xhalf_max(mx) + m_acc[rb];
-      else mx = xhalf_max(mx) * c;                   // log2 units
+      mx = xhalf_max(mx) * c;                   // log2 units
       const bool grow = mx > m_use[rb] + kLazyRescale;
       if (__builtin_amdgcn_ballot_w64(grow)) {
         asm volatile("" ::: "memory");   // rare: keep the O rescale out of the common path
@@ -398,15 +369,6 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
         for (int i = 0; i < DVB; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[rb][i][r] *= alpha;
-        if constexpr (QS) {   // move this tile's scores and later accumulators to the new reference
-          const float ms = (m_use[rb] == -__builtin_inff()) ? 0.f : m_use[rb];
-          const float d = ms - m_acc[rb];
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sc[rb][kb][r] -= d;
-          m_acc[rb] = ms;
-        }
       }
       const float msub = (m_use[rb] == -__builtin_inff()) ? 0.f : m_use[rb];
       float lsum = l_run[rb];
@@ -414,8 +376,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
       for (int kb = 0; kb < NKB; ++kb) {
         float p[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          p[r] = QS ? fast_exp2(sc[rb][kb][r]) : fast_exp2(__builtin_fmaf(sc[rb][kb][r], c, -msub));
+        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(__builtin_fmaf(sc[rb][kb][r], c, -msub));
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) {
           u32x4 v;
@@ -570,22 +531,12 @@ static hipError_t launch_cfg(const AttnArgs& a0, bool fastc, hipStream_t st) {
   if (units <= 0) return hipSuccess;
   a.xcd_remap = (units % 8 == 0) ? 1 : 0;
   const dim3 grid((unsigned)units), block(64 * NR * NS);
-  // q scaling pays at head size 64 without a mask band (measured); q * c must
-  // stay in the input type's range
-  constexpr bool QS_OK = DQK == 64 && !CAUSAL && !WIN && !F8;
-  if constexpr (QS_OK) {
-    if (fastc && a.c <= 1.f) {
-      hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, WIN, RB, NR, NS, BN, PAIR, true, MINW, F8, ROTQ, true>),
-                         grid, block, 0, st, a);
-      return hipGetLastError();
-    }
-  }
   if (fastc)
-    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, WIN, RB, NR, NS, BN, PAIR, true, MINW, F8, ROTQ, false>),
-                       grid, block, 0, st, a);
+    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, WIN, RB, NR, NS, BN, PAIR, true, MINW, F8, ROTQ>), grid,
+                       block, 0, st, a);
   else
-    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, WIN, RB, NR, NS, BN, PAIR, false, MINW, F8, ROTQ, false>),
-                       grid, block, 0, st, a);
+    hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, WIN, RB, NR, NS, BN, PAIR, false, MINW, F8, ROTQ>), grid,
+                       block, 0, st, a);
   return hipGetLastError();
 }
 

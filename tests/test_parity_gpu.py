@@ -140,6 +140,32 @@ def test_fwd_softmax_scale_zero_is_mean():
     _fwd_check(case)
 
 
+@pytest.mark.parametrize("scale", [1.0, 1.5, -0.1])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_fwd_d64_scale_values(scale, dtype):
+    # positive scales up to and beyond 1 take the fast path, non-positive ones the general path
+    case = W.random_fwd(1, 200, 333, 2, 2, 64, 64, dtype, False, seed=11, softmax_scale=scale)
+    _fwd_check(case, return_lse=True)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_fwd_d64_growing_scores(dtype):
+    # scores grow along the keys (|lse| up to 15), so rows raise their running max on many
+    # key tiles; large scores also expose any rounding of q or of the scaled scores
+    case = W.random_fwd(1, 130, 700, 2, 2, 64, 64, dtype, False, seed=12)
+    ramp = torch.linspace(0.5, 4.0, 700).view(1, 700, 1, 1)
+    case.k = (case.k.float() * ramp).to(case.k.dtype)
+    _fwd_check(case, return_lse=True)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_fwd_d64_large_queries(dtype):
+    # q three times the unit normal: scores of tens, as in trained models
+    case = W.random_fwd(1, 256, 512, 2, 2, 64, 64, dtype, False, seed=5)
+    case.q = (case.q.float() * 3).to(case.q.dtype)
+    _fwd_check(case, return_lse=True)
+
+
 def test_fwd_ones_v_gives_ones():
     # probabilities sum to one: V = 1 gives O = 1 for every row
     case = W.random_fwd(1, 130, 130, 2, 1, 128, 128, "bf16", True, seed=4)
