@@ -551,6 +551,13 @@ def test_bwd_multi_tile_ragged(dqk, dv, dtype, causal):
     _bwd_check(case, seed=dqk)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_workload_bwd_d64_full(causal):
+    # every gradient element at the shape and launch configuration the benchmark times
+    # (B=2, H=8, S=2048, D=64 fp16); the fp64 oracle takes a few seconds here
+    _bwd_check(W.fwd_d64(causal), seed=11)
+
+
 @pytest.mark.parametrize("sq,sk", [(100, 333), (333, 100), (1, 70), (70, 1)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_sq_ne_sk(sq, sk, causal):
