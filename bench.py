@@ -1,18 +1,22 @@
 """Benchmark: exact attention prefill TFLOP/s and KV-cache decode GB/s on one MI355X.
 
-One JSON line is printed.  ``value`` is the prefill throughput of the headline
-workload: attn_fwd on B=2, H=8, S=2048, D=64, fp16 (N(0,1) inputs, scale
-1/8), one non-causal and one causal call per step; algorithmic work
-2*(Dqk+Dv) flop per unmasked (query, key) pair.  The same line carries the
-decode throughput (KV bytes read per second) of the single-token GQA decode
-workload, every other workload's timing, the roofline entry of the dominant
-kernel and the fp64 CPU oracle's throughput on a bounded sample.
+One JSON line is printed.  ``value`` is the prefill throughput of the largest
+configuration that fits one GPU: causal attn_fwd on B=2, H=16, S=4096,
+head_dim_qk=192, head_dim_v=128, bf16, N(0,1) inputs, scale 1/sqrt(192)
+(flash-attention PR #1604's head sizes); algorithmic work is 2*(Dqk+Dv) flop
+per unmasked (query, key) pair, 171.84 GFLOP per call.  A step is one such
+call.  The same line carries every other configuration ("configs": the
+empty-cache kvcache call, attn_fwd B=2 H=8 S=2048 D=64 fp16 non-causal and
+causal, the GQA single-token decode, the chunked prefill) with its own
+roofline entry, the extra rows (local window, packed sequences, backward,
+FP8 inputs), the peaks re-derived from rocminfo, and the fp64 CPU oracle's
+timing together with each configuration's error against it.
 
-Inputs are resident in HBM before the timed region.  GPU time comes from HIP
-events recorded on the stream the library launches on (torch's current
-stream), around back-to-back calls.  Decode and chunked-prefill calls cycle
-through 4 input/cache replicas so each call reads HBM rather than the 256 MB
-Infinity Cache.
+GPU time comes from HIP events recorded on the stream the library launches
+on (torch's current stream), around back-to-back calls, with inputs already
+resident in HBM.  The headline, decode and chunked-prefill calls cycle through
+input replicas (2, 4 and 4) whose total exceeds the 256 MB Infinity Cache, so
+each call reads HBM rather than that cache.
 """
 from __future__ import annotations
 
@@ -20,18 +24,32 @@ import argparse
 import json
 import math
 import os
+import re
+import subprocess
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = 2516.6     # dense fp16/bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
-PEAK_HBM_GBS = 8000.0    # HBM3E
-PEAK_FP8_TFLOPS = 5033.2  # dense fp8 MFMA (twice the fp16 rate)
-# FP8-input attention runs Q K^T in fp8 and P V in bf16 (half of the flops each)
-PEAK_FP8_BLEND = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_TFLOPS)
 METRIC = "attn prefill TFLOP/s + decode KV GB/s at 1 GPU, as % of MI355X peak"
+# Published MI355X figures, used when rocminfo is not available.
+PUB_CUS, PUB_MHZ = 256, 2400
+FLOP_PER_CLK_CU_BF16 = 4096   # v_mfma_f32_32x32x16_bf16: 32768 flop per 32 cycles per SIMD, 4 SIMDs per CU
+PEAK_HBM_GBS = 8000.0         # HBM3E, 8 stacks (rocminfo lists no memory bandwidth)
+
+TILE_SRCS = ["exact_attention_qk_amd/csrc/tile_attn.hip", "exact_attention_qk_amd/csrc/device_common.hpp",
+             "exact_attention_qk_amd/csrc/attn_args.hpp", "exact_attention_qk_amd/csrc/launchers.hpp"]
+DECODE_SRCS = ["exact_attention_qk_amd/csrc/decode_attn.hip", "exact_attention_qk_amd/csrc/device_common.hpp",
+               "exact_attention_qk_amd/csrc/attn_args.hpp", "exact_attention_qk_amd/csrc/launchers.hpp"]
+# dominant kernel of each configuration: a pattern of its rocprofv3 name, and its sources
+DOMINANT = {
+    "C5_fwd_asym_b2h16s4096_causal": (r"tile_attn_kernel<attn::BF16, 192, 128, true, false,", TILE_SRCS),
+    "C2_fwd_b2h8s2048d64": (r"tile_attn_kernel<attn::F16, 64, 64, false, false,", TILE_SRCS),
+    "C2_fwd_b2h8s2048d64_causal": (r"tile_attn_kernel<attn::F16, 64, 64, true, false,", TILE_SRCS),
+    "C3_decode_gqa": (r"decode_attn_kernel<attn::BF16, 128, 128,", DECODE_SRCS),
+    "C4_chunked_prefill": (r"tile_attn_kernel<attn::BF16, 128, 128, true, false,", TILE_SRCS),
+}
 
 
 def parse():
@@ -41,17 +59,48 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
-                    help="comma list of extra workloads to time: decode, chunked, window, bwd, varlen, fp8, asym, empty "
-                         "(default: all; 'none' times the headline only)")
+                    help="comma list of configurations / rows to time besides the headline: "
+                         "c1, c2, c3, c4, window, bwd, varlen, fp8 (default: all; 'none': the headline only)")
     ap.add_argument("--copy-mib", type=int, default=0,
-                    help="also run a plain device copy of this many MiB (counter calibration)")
+                    help="also run a plain device copy of this many MiB (calibrates the HBM byte counters)")
     ap.add_argument("--summarize", default="",
                     help="print a text summary of a rocprofv3 CSV output directory and exit")
+    ap.add_argument("--record-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_MIB"),
+                    help="write profiles/traffic.json from a FETCH_SIZE and a WRITE_SIZE rocprofv3 run "
+                         "of this script (both with --copy-mib COPY_MIB) and exit")
     return ap.parse_args()
 
 
+# ---------------------------------------------------------------- peaks
+
+def peaks():
+    """Compute units and peak engine clock of the gfx950 agent from rocminfo; the dense
+    bf16/fp16 MFMA peak follows from the per-CU rate of the instruction set."""
+    cus, mhz, src = PUB_CUS, PUB_MHZ, "published (rocminfo unavailable)"
+    try:
+        txt = subprocess.run(["rocminfo"], stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True,
+                             timeout=60).stdout
+        for agent in txt.split("*******")[1:]:
+            if "gfx950" not in agent:
+                continue
+            cu = re.search(r"Compute Unit:\s+(\d+)", agent)
+            mc = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", agent)
+            if cu and mc:
+                cus, mhz, src = int(cu.group(1)), int(mc.group(1)), "rocminfo (gfx950 agent)"
+                break
+    except Exception:
+        pass
+    mfma = cus * FLOP_PER_CLK_CU_BF16 * mhz * 1e6 / 1e12
+    return {"compute_units": cus, "max_clock_mhz": mhz, "source": src,
+            "mfma_bf16_tflops": mfma, "mfma_fp8_tflops": 2 * mfma,
+            "hbm_gbs": PEAK_HBM_GBS, "hbm_source": "published HBM3E figure"}
+
+
+# ---------------------------------------------------------------- timing
+
 def time_loop(calls, steps, warmup, torch):
-    """Average seconds per call over `steps` back-to-back calls (cycling through `calls`)."""
+    """Average seconds per call over `steps` back-to-back calls (cycling through `calls`),
+    from HIP events on the stream the calls enqueue on."""
     n = len(calls)
     for i in range(warmup):
         calls[i % n]()
@@ -66,6 +115,14 @@ def time_loop(calls, steps, warmup, torch):
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / 1e3 / steps
 
+
+def mfma_entry(name, fl, t, pk, kernel):
+    a = fl / t / 1e12
+    return {"kernel": kernel, "bound": "mfma", "achieved": a, "peak": pk["mfma_bf16_tflops"], "unit": "TFLOP/s",
+            "frac": a / pk["mfma_bf16_tflops"], "traffic": traffic_entry(name), "avg_launch_us": t * 1e6}
+
+
+# ---------------------------------------------------------------- rocprofv3 helpers
 
 def summarize(d):
     """Text summary of rocprofv3 CSV output: kernel durations and per-dispatch counters."""
@@ -84,13 +141,25 @@ def summarize(d):
         for r in csv.DictReader(open(path)):
             agg[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
         for k, cs in agg.items():
-            print(k[:120])
+            print(k[:140])
             for cn, v in sorted(cs.items()):
                 print("    %-32s %16.6g   (dispatches: %d)" % (cn, sum(v) / len(v), len(v)))
 
 
+def _counter_means(d, counter):
+    import csv
+    import glob
+    from collections import defaultdict
+    acc = defaultdict(list)
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
 def sources_sha256(paths):
-    """One digest over the given source files (the kernel file and the headers it includes)."""
+    """One digest over the given source files (a kernel file and the headers it includes)."""
     import hashlib
     h = hashlib.sha256()
     for p in paths:
@@ -99,12 +168,36 @@ def sources_sha256(paths):
     return h.hexdigest()
 
 
-def traffic_entry(kernel_key):
-    """Measured HBM bytes per launch for a kernel, if its sources are unchanged since measured."""
+def record_traffic(fetch_dir, write_dir, copy_mib):
+    """HBM bytes per launch of each configuration's dominant kernel: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) scaled by what they read for a plain copy of
+    copy_mib MiB (which reads and writes exactly that many bytes)."""
+    fetch, write = _counter_means(fetch_dir, "FETCH_SIZE"), _counter_means(write_dir, "WRITE_SIZE")
+    cp = [k for k in fetch if "copyBuffer" in k]
+    assert cp, "no copy kernel in the FETCH_SIZE run (run it with --copy-mib)"
+    moved_kib = int(copy_mib) * 1024.0
+    fs, ws = moved_kib / fetch[cp[0]], moved_kib / write[cp[0]]
+    out = {"_calibration": {"copy_mib": int(copy_mib), "fetch_scale": fs, "write_scale": ws}}
+    for name, (pat, srcs) in DOMINANT.items():
+        ks = sorted({k for k in fetch if re.search(pat, k)})
+        if len(ks) != 1 or ks[0] not in write:
+            continue
+        k = ks[0]
+        out[name] = {"kernel": k, "sources": srcs, "sources_sha256": sources_sha256(srcs),
+                     "fetch_kib_per_dispatch": fetch[k], "write_kib_per_dispatch": write[k],
+                     "hbm_bytes_per_launch": 1024.0 * (fetch[k] * fs + write[k] * ws)}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    json.dump(out, open(path, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def traffic_entry(name):
+    """Measured HBM bytes per launch of a configuration's dominant kernel, if its
+    sources are unchanged since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get(kernel_key)
+    rec = json.load(open(path)).get(name)
     if not rec:
         return None
     srcs = rec.get("sources", [])
@@ -115,10 +208,15 @@ def traffic_entry(kernel_key):
     return rec["hbm_bytes_per_launch"]
 
 
+# ---------------------------------------------------------------- main
+
 def main():
     args = parse()
     if args.summarize:
         summarize(args.summarize)
+        return
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -134,81 +232,121 @@ def main():
     dev = "cuda"
     K, Wm = args.steps, args.warmup
     only = set(x for x in args.only.split(",") if x)
-    results = {}
+    pk = peaks()
+    configs, rows, outputs = {}, {}, {}
 
     def want(name):
-        return not only or name in only   # "none" matches no workload
+        return not only or name in only   # "none" matches nothing
 
-    # ---------------- headline: attn_fwd B=2 H=8 S=2048 D=64 fp16, non-causal + causal
-    hl = {}
-    for causal in (False, True):
-        c = W.fwd_d64(causal)
+    # ---------------- C5 (headline): causal B=2 H=16 S=4096 Dqk=192 Dv=128 bf16, 2 replicas
+    c = W.fwd_asym()
+    calls, outs = [], []
+    for r in range(2):
         q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
-        out = torch.empty_like(q)
-        call = E.prepare_fwd(q, k, v, out, causal, c.softmax_scale)
-        t = time_loop([call], K, Wm, torch)
-        fl = W.fwd_flops(2, 2048, 2048, 8, 64, 64, causal)
-        hl[causal] = (t, fl)
-        results["fwd_b2h8s2048d64" + ("_causal" if causal else "")] = {
-            "us": t * 1e6, "gflop": fl / 1e9, "tflops": fl / t / 1e12,
-            "pct_mfma_peak": 100 * fl / t / 1e12 / PEAK_TFLOPS}
-    step_s = hl[False][0] + hl[True][0]
-    step_flops = hl[False][1] + hl[True][1]
-    value = step_flops / step_s / 1e12
+        out = torch.empty((2, 4096, 16, 128), dtype=q.dtype, device=dev)
+        calls.append(E.prepare_fwd(q, k, v, out, True, c.softmax_scale))
+        outs.append(out)
+    t5 = time_loop(calls, K, Wm, torch)
+    t5_one = time_loop(calls[:1], K, Wm, torch)
+    fl5 = W.fwd_flops(2, 4096, 4096, 16, 192, 128, True)
+    name5 = "C5_fwd_asym_b2h16s4096_causal"
+    configs[name5] = {"us": t5 * 1e6, "us_same_inputs": t5_one * 1e6, "gflop": fl5 / 1e9,
+                      "tflops": fl5 / t5 / 1e12, "pct_mfma_peak": 100 * fl5 / t5 / 1e12 / pk["mfma_bf16_tflops"],
+                      "roofline": mfma_entry(name5, fl5, t5, pk, "tile_attn_kernel<BF16,192,128,causal>")}
+    outputs[name5] = outs[0].cpu()
+    del calls, outs, q, k, v, out
+    torch.cuda.empty_cache()
 
-    # ---------------- decode: GQA 32/8, D=128, bf16, RoPE rd=128, cache 8192 (4 replicas)
-    decode = None
-    if want("decode"):
-        c = W.decode_gqa()
-        lens = W.seqlens_list(c.cache_seqlens, 8)
-        calls = []
-        cs = c.cache_seqlens.to(dev)
-        cos, sin = c.rotary_cos.to(dev), c.rotary_sin.to(dev)
-        q, kn, vn = c.q.to(dev), c.k_new.to(dev), c.v_new.to(dev)
+    # ---------------- C1: empty-cache kvcache (latency only)
+    if want("c1"):
+        c1 = W.kvcache_empty()
+        q = c1.q.to(dev)
+        kc, vc = c1.k_cache.to(dev), c1.v_cache.to(dev)
+        out = torch.empty((4, 2, 16, 16), dtype=q.dtype, device=dev)
+        call = E.prepare_kvcache(q, kc, vc, q, q, out, cache_seqlens=0)
+        t = time_loop([call], K, Wm, torch)
+        configs["C1_kvcache_empty"] = {"us": t * 1e6, "bound": "latency"}
+        outputs["C1_kvcache_empty"] = out.cpu()
+
+    # ---------------- C2: attn_fwd B=2 H=8 S=2048 D=64 fp16, non-causal and causal
+    if want("c2"):
+        for causal in (False, True):
+            c2 = W.fwd_d64(causal)
+            q, k, v = c2.q.to(dev), c2.k.to(dev), c2.v.to(dev)
+            out = torch.empty_like(q)
+            call = E.prepare_fwd(q, k, v, out, causal, c2.softmax_scale)
+            t = time_loop([call], K, Wm, torch)
+            fl = W.fwd_flops(2, 2048, 2048, 8, 64, 64, causal)
+            nm = "C2_fwd_b2h8s2048d64" + ("_causal" if causal else "")
+            configs[nm] = {"us": t * 1e6, "gflop": fl / 1e9, "tflops": fl / t / 1e12,
+                           "pct_mfma_peak": 100 * fl / t / 1e12 / pk["mfma_bf16_tflops"],
+                           "roofline": mfma_entry(nm, fl, t, pk, "tile_attn_kernel<F16,64,64,%s>"
+                                                  % ("causal" if causal else "non-causal"))}
+            outputs[nm] = out.cpu()
+            del call, q, k, v, out
+
+    # ---------------- C3: decode, GQA 32/8, D=128, bf16, RoPE rd=128, cache 8192 (4 replicas)
+    if want("c3"):
+        c3 = W.decode_gqa()
+        lens = W.seqlens_list(c3.cache_seqlens, 8)
+        cs = c3.cache_seqlens.to(dev)
+        cos, sin = c3.rotary_cos.to(dev), c3.rotary_sin.to(dev)
+        q, kn, vn = c3.q.to(dev), c3.k_new.to(dev), c3.v_new.to(dev)
+        calls, outs = [], []
         for r in range(4):
-            kc, vc = c.k_cache.to(dev), c.v_cache.to(dev)
+            kc, vc = c3.k_cache.to(dev), c3.v_cache.to(dev)
             out = torch.empty((8, 1, 32, 128), dtype=q.dtype, device=dev)
             calls.append(E.prepare_kvcache(q, kc, vc, kn, vn, out, rotary_cos=cos, rotary_sin=sin,
                                            cache_seqlens=cs, causal=True,
-                                           softmax_scale=c.softmax_scale, rotary_interleaved=False))
-        del c
+                                           softmax_scale=c3.softmax_scale, rotary_interleaved=False))
+            outs.append(out)
         t = time_loop(calls, K, Wm, torch)
         kv_bytes = sum(L + 1 for L in lens) * 8 * (128 + 128) * 2
         other = (8 * 32 * 128 * 2) * 2 + (8 * 8 * 128 * 2) * 4
-        decode = {"workload": "attn_fwd_kvcache decode B=8 Hq=32 Hkv=8 D=128 bf16 cap=8192 "
-                              "RoPE rd=128 non-interleaved, seqlens seed 0",
-                  "us": t * 1e6, "kv_bytes": kv_bytes, "gbs": kv_bytes / t / 1e9,
-                  "gbs_all_bytes": (kv_bytes + other) / t / 1e9,
-                  "pct_hbm_peak": 100 * kv_bytes / t / 1e9 / PEAK_HBM_GBS}
-        results["decode_gqa"] = decode
-        del calls
+        a = kv_bytes / t / 1e9
+        configs["C3_decode_gqa"] = {
+            "us": t * 1e6, "kv_bytes": kv_bytes, "gbs": a, "gbs_all_bytes": (kv_bytes + other) / t / 1e9,
+            "pct_hbm_peak": 100 * a / pk["hbm_gbs"], "seqlens": lens,
+            "roofline": {"kernel": "decode_attn_kernel<BF16,128,128> + split_merge_kernel (whole call)",
+                         "bound": "hbm", "achieved": a, "peak": pk["hbm_gbs"], "unit": "GB/s",
+                         "frac": a / pk["hbm_gbs"], "traffic": traffic_entry("C3_decode_gqa"),
+                         "avg_launch_us": t * 1e6}}
+        outputs["C3_decode_gqa"] = outs[0].cpu()
+        del calls, outs, kc, vc
         torch.cuda.empty_cache()
 
-    # ---------------- chunked prefill: B=4 H=16 D=128 bf16, 512 new tokens, RoPE rd=64 interleaved
-    if want("chunked"):
-        c = W.chunked_prefill()
-        lens = W.seqlens_list(c.cache_seqlens, 4)
-        cs = c.cache_seqlens.to(dev)
-        cos, sin = c.rotary_cos.to(dev), c.rotary_sin.to(dev)
-        calls = []
+    # ---------------- C4: chunked prefill B=4 H=16 D=128 bf16, 512 new tokens, RoPE rd=64 interleaved
+    if want("c4"):
+        c4 = W.chunked_prefill()
+        lens = W.seqlens_list(c4.cache_seqlens, 4)
+        cs = c4.cache_seqlens.to(dev)
+        cos, sin = c4.rotary_cos.to(dev), c4.rotary_sin.to(dev)
+        calls, outs = [], []
         for r in range(4):
-            q, kn, vn = c.q.to(dev), c.k_new.to(dev), c.v_new.to(dev)
-            kc, vc = c.k_cache.to(dev), c.v_cache.to(dev)
+            q, kn, vn = c4.q.to(dev), c4.k_new.to(dev), c4.v_new.to(dev)
+            kc, vc = c4.k_cache.to(dev), c4.v_cache.to(dev)
             out = torch.empty_like(q)
             calls.append(E.prepare_kvcache(q, kc, vc, kn, vn, out, rotary_cos=cos, rotary_sin=sin,
                                            cache_seqlens=cs, causal=True,
-                                           softmax_scale=c.softmax_scale, rotary_interleaved=True))
-        del c
+                                           softmax_scale=c4.softmax_scale, rotary_interleaved=True))
+            outs.append(out)
         t = time_loop(calls, K, Wm, torch)
         fl = 2.0 * 256 * 16 * W.kvcache_pairs(lens, 512, 512, True)
         byt = sum(lens) * 16 * 256 * 2 + 3 * 4 * 512 * 16 * 256 * 2
-        results["chunked_prefill"] = {"us": t * 1e6, "gflop": fl / 1e9, "tflops": fl / t / 1e12,
-                                      "pct_mfma_peak": 100 * fl / t / 1e12 / PEAK_TFLOPS,
-                                      "gbs": byt / t / 1e9, "pct_hbm_peak": 100 * byt / t / 1e9 / PEAK_HBM_GBS}
-        del calls
+        a = fl / t / 1e12
+        configs["C4_chunked_prefill"] = {
+            "us": t * 1e6, "gflop": fl / 1e9, "tflops": a, "pct_mfma_peak": 100 * a / pk["mfma_bf16_tflops"],
+            "bytes": byt, "gbs": byt / t / 1e9, "pct_hbm_peak": 100 * byt / t / 1e9 / pk["hbm_gbs"],
+            "seqlens": lens,
+            "roofline": {"kernel": "rope append + tile_attn_kernel<BF16,128,128,causal> (whole call)",
+                         "bound": "mfma", "achieved": a, "peak": pk["mfma_bf16_tflops"], "unit": "TFLOP/s",
+                         "frac": a / pk["mfma_bf16_tflops"], "traffic": traffic_entry("C4_chunked_prefill"),
+                         "avg_launch_us": t * 1e6, "hbm_frac": byt / t / 1e9 / pk["hbm_gbs"]}}
+        outputs["C4_chunked_prefill"] = outs[0].cpu()
+        del calls, outs, q, kn, vn, kc, vc
         torch.cuda.empty_cache()
 
-    # ---------------- local window: the headline shape with window_size=(256, 256), causal
+    # ---------------- extra rows
     if want("window"):
         c = W.fwd_d64(True)
         q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
@@ -216,12 +354,11 @@ def main():
         call = E.prepare_fwd(q, k, v, out, True, c.softmax_scale, window_size=(256, 256))
         t = time_loop([call], K, Wm, torch)
         fl = W.fwd_flops(2, 2048, 2048, 8, 64, 64, True, window=(256, 256))
-        results["fwd_b2h8s2048d64_causal_window256"] = {
+        rows["fwd_b2h8s2048d64_causal_window256"] = {
             "us": t * 1e6, "gflop": fl / 1e9, "tflops": fl / t / 1e12,
-            "pct_mfma_peak": 100 * fl / t / 1e12 / PEAK_TFLOPS}
+            "pct_mfma_peak": 100 * fl / t / 1e12 / pk["mfma_bf16_tflops"]}
         del call, q, k, v, out, c
 
-    # ---------------- gradients on the headline shape (dq, dk, dv from dO), non-causal and causal
     if want("bwd"):
         for causal in (False, True):
             c = W.fwd_d64(causal)
@@ -233,12 +370,11 @@ def main():
             call = E.prepare_bwd(dout, q, k, v, out, lse, dq, dk, dv, causal, c.softmax_scale)
             t = time_loop([call], K, Wm, torch)
             fl = W.bwd_flops(2, 2048, 2048, 8, 64, 64, causal)
-            results["bwd_b2h8s2048d64" + ("_causal" if causal else "")] = {
+            rows["bwd_b2h8s2048d64" + ("_causal" if causal else "")] = {
                 "us": t * 1e6, "gflop": fl / 1e9, "tflops": fl / t / 1e12,
-                "pct_mfma_peak": 100 * fl / t / 1e12 / PEAK_TFLOPS}
+                "pct_mfma_peak": 100 * fl / t / 1e12 / pk["mfma_bf16_tflops"]}
             del call, q, k, v, out, lse, dout, dq, dk, dv, c
 
-    # ---------------- packed sequences: the headline token budget (2 x 2048) as 7 seeded lengths
     if want("varlen"):
         lens = W.packed_lengths(4096, 7, seed=0)
         c = W.random_varlen(lens, lens, 8, 8, 64, 64, "fp16", True, seed=0)
@@ -248,13 +384,13 @@ def main():
         call = E.prepare_varlen(q, k, v, out, cq, ck, c.max_seqlen_q, True, 0.125)
         t = time_loop([call], K, Wm, torch)
         fl = sum(W.fwd_flops(1, n, n, 8, 64, 64, True) for n in lens)
-        results["varlen_7seq_4096tok_h8d64_causal"] = {
+        rows["varlen_7seq_4096tok_h8d64_causal"] = {
             "us": t * 1e6, "gflop": fl / 1e9, "tflops": fl / t / 1e12,
-            "pct_mfma_peak": 100 * fl / t / 1e12 / PEAK_TFLOPS, "lengths": lens}
+            "pct_mfma_peak": 100 * fl / t / 1e12 / pk["mfma_bf16_tflops"], "lengths": lens}
         del call, q, k, v, out, c
 
-    # ---------------- FP8 (e4m3) inputs on the headline shape, non-causal and causal
     if want("fp8"):
+        blend = 1.0 / (0.5 / pk["mfma_fp8_tflops"] + 0.5 / pk["mfma_bf16_tflops"])
         for causal in (False, True):
             c = W.fwd_fp8_d64(causal)
             q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
@@ -262,98 +398,132 @@ def main():
             call = E.prepare_fp8(q, k, v, out, causal, None)
             t = time_loop([call], K, Wm, torch)
             fl = W.fwd_flops(2, 2048, 2048, 8, 64, 64, causal)
-            results["fwd_fp8_b2h8s2048d64" + ("_causal" if causal else "")] = {
+            rows["fwd_fp8_b2h8s2048d64" + ("_causal" if causal else "")] = {
                 "us": t * 1e6, "gflop": fl / 1e9, "tflops": fl / t / 1e12,
-                "pct_blended_peak": 100 * fl / t / 1e12 / PEAK_FP8_BLEND,
-                "peak_note": "QK^T on fp8 MFMA, PV on bf16 MFMA: blended peak %.0f TFLOP/s" % PEAK_FP8_BLEND}
+                "pct_blended_peak": 100 * fl / t / 1e12 / blend,
+                "peak_note": "Q K^T on fp8 MFMA, P V on bf16 MFMA: blended peak %.0f TFLOP/s" % blend}
             del call, q, k, v, out, c
 
-    # ---------------- asymmetric head dims: B=2 H=16 S=4096 Dqk=192 Dv=128 bf16 causal
-    if want("asym"):
-        c = W.fwd_asym()
-        q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
-        out = torch.empty((2, 4096, 16, 128), dtype=q.dtype, device=dev)
-        call = E.prepare_fwd(q, k, v, out, True, c.softmax_scale)
-        t = time_loop([call], max(5, K // 5), max(2, Wm // 5), torch)
-        fl = W.fwd_flops(2, 4096, 4096, 16, 192, 128, True)
-        results["fwd_asym_b2h16s4096"] = {"us": t * 1e6, "gflop": fl / 1e9, "tflops": fl / t / 1e12,
-                                          "pct_mfma_peak": 100 * fl / t / 1e12 / PEAK_TFLOPS}
-        del call, q, k, v, out, c
-
-    # ---------------- empty-cache kvcache (latency only)
-    if want("empty"):
-        c = W.kvcache_empty()
-        q = c.q.to(dev)
-        kc, vc = c.k_cache.to(dev), c.v_cache.to(dev)
-        out = torch.empty((4, 2, 16, 16), dtype=q.dtype, device=dev)
-        call = E.prepare_kvcache(q, kc, vc, q, q, out, cache_seqlens=0)
-        t = time_loop([call], K, Wm, torch)
-        results["kvcache_empty"] = {"us": t * 1e6}
-
-    # ---------------- plain copy (calibrates the HBM byte counters)
     if args.copy_mib:
         src = torch.empty(args.copy_mib * 2**20 // 2, dtype=torch.bfloat16, device=dev)
         dst = torch.empty_like(src)
         t = time_loop([lambda: dst.copy_(src)], K, Wm, torch)
-        results["copy_%dmib" % args.copy_mib] = {"us": t * 1e6, "gbs_read_plus_write":
-                                                 2 * args.copy_mib * 2**20 / t / 1e9}
+        rows["copy_%dmib" % args.copy_mib] = {"us": t * 1e6,
+                                              "gbs_read_plus_write": 2 * args.copy_mib * 2**20 / t / 1e9}
         del src, dst
 
-    # ---------------- roofline entry: the non-causal headline kernel
-    t_nc, fl_nc = hl[False]
-    roofline = {"kernel": "tile_attn_kernel<F16,64,64,non-causal>", "bound": "mfma",
-                "achieved": fl_nc / t_nc / 1e12, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": fl_nc / t_nc / 1e12 / PEAK_TFLOPS,
-                "traffic": traffic_entry("tile_attn_fwd_b2h8s2048d64"),
-                "avg_launch_us": t_nc * 1e6,
-                "algorithmic": "2*(64+64) flop x 2*8*2048*2048 (query,key) pairs = %.4g GFLOP per launch"
-                               % (fl_nc / 1e9)}
-
-    # ---------------- CPU oracle on the headline workload
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline()
+        cpu = cpu_baseline(outputs)
 
+    h = configs[name5]
     line = {
-        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": Wm,
-        "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
-        "config": {"workload": "attn_fwd B=2 H=8 S=2048 D=64 fp16 N(0,1) scale 1/8, "
-                               "one non-causal + one causal call per step",
-                   "global_batch": 2, "seq_len": 2048, "heads": 8, "head_dim": 64,
+        "metric": METRIC, "value": h["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": t5 * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "attn_fwd causal B=2 H=16 S=4096 head_dim_qk=192 head_dim_v=128 bf16, "
+                               "q/k/v N(0,1) seed 0, scale 1/sqrt(192); one call per step, 2 input replicas",
+                   "global_batch": 2, "seq_len": 4096, "heads": 16, "head_dim_qk": 192, "head_dim_v": 128,
                    "parallelism": "single-gpu"},
-        "pct_mfma_peak": 100 * value / PEAK_TFLOPS,
-        "decode": decode,
-        "roofline": roofline,
+        "pct_mfma_peak": h["pct_mfma_peak"],
+        "roofline": dict(h["roofline"], algorithmic="2*(192+128) flop x 2*16*4096*4097/2 unmasked (query,key) "
+                                                    "pairs = %.5g GFLOP per launch" % (fl5 / 1e9)),
+        "decode": configs.get("C3_decode_gqa"),
+        "peaks": pk,
         "cpu_baseline": cpu,
-        "workloads": results,
+        "configs": configs,
+        "rows": rows,
     }
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline():
-    """The fp64 oracle, as it stands, on the headline step (both masks), repeated to ~10 s."""
+# ---------------------------------------------------------------- CPU oracle leg
+
+def _ulp(ref, dtype):
+    """Spacing of the target format at each reference value (normal range; subnormals
+    share the smallest normal's spacing)."""
+    import numpy as np
+    mant, emin = (10, -14) if dtype == "fp16" else (7, -126)
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, emin)
+    return np.exp2(e - mant)
+
+
+def _errors(got, ref, dtype):
+    import numpy as np
+    from oracle import to_f64
+    g = to_f64(got.float())
+    d = np.abs(g - ref)
+    u = d / _ulp(ref, dtype)
+    return {"max_abs_err": float(d.max()), "max_ulp_err": float(u.max()),
+            "p999_ulp_err": float(np.quantile(u, 0.999)), "frac_within_1ulp": float((u <= 1.0).mean()),
+            "elements": int(d.size)}
+
+
+def cpu_baseline(outputs):
+    """The fp64 oracle, as it stands, timed on this host on every configuration the
+    run timed (each once, whole), and compared with the GPU output of that run."""
+    import numpy as np
+    import torch
     import workloads as W
-    from oracle import attention_ref, to_f64
+    from oracle import attention_ref, kvcache_ref, to_f64
     try:
         from threadpoolctl import threadpool_info
-        cores = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else 1
+        info = threadpool_info()
+        cores = max(i.get("num_threads", 1) for i in info) if info else 1
     except Exception:
         cores = os.cpu_count() or 1
-    cases = [W.fwd_d64(False), W.fwd_d64(True)]
-    arrs = [(to_f64(c.q), to_f64(c.k), to_f64(c.v), c.causal, c.softmax_scale) for c in cases]
-    flops = sum(W.fwd_flops(2, 2048, 2048, 8, 64, 64, c.causal) for c in cases)
-    reps, t_tot = 0, 0.0
-    while reps < 8 and t_tot < 10.0:
+    per = {}
+
+    def fwd(name, case, fl):
+        qf, kf, vf = to_f64(case.q), to_f64(case.k), to_f64(case.v)
         t0 = time.perf_counter()
-        for q, k, v, causal, sc in arrs:
-            attention_ref(q, k, v, causal=causal, softmax_scale=sc)
-        t_tot += time.perf_counter() - t0
-        reps += 1
-    return {"value": flops * reps / t_tot / 1e12, "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
-            "sample": "full headline step (non-causal + causal attn_fwd, B=2 H=8 S=2048 D=64) "
-                      "x%d, fp64 numpy, %.1f s" % (reps, t_tot)}
+        ref, _ = attention_ref(qf, kf, vf, causal=case.causal, softmax_scale=case.softmax_scale)
+        dt = time.perf_counter() - t0
+        per[name] = dict(_errors(outputs[name], ref, case.dtype), oracle_s=dt, oracle_tflops=fl / dt / 1e12)
+
+    def kv(name, case, work_key, work):
+        B = case.q.shape[0]
+        lens = W.seqlens_list(case.cache_seqlens, B)
+        f = to_f64
+        args = (f(case.q), f(case.k_cache), f(case.v_cache), f(case.k_new), f(case.v_new),
+                lens if isinstance(case.cache_seqlens, torch.Tensor) else case.cache_seqlens)
+        kw = dict(dtype=case.dtype, rotary_interleaved=case.rotary_interleaved, causal=case.causal,
+                  softmax_scale=case.softmax_scale,
+                  rotary_cos=None if case.rotary_cos is None else f(case.rotary_cos),
+                  rotary_sin=None if case.rotary_sin is None else f(case.rotary_sin))
+        t0 = time.perf_counter()
+        ref = kvcache_ref(*args, **kw)[0]
+        dt = time.perf_counter() - t0
+        e = dict(_errors(outputs[name], ref, case.dtype), oracle_s=dt)
+        if work_key:
+            e[work_key] = work / dt
+        per[name] = e
+
+    name5 = "C5_fwd_asym_b2h16s4096_causal"
+    fl5 = W.fwd_flops(2, 4096, 4096, 16, 192, 128, True)
+    fwd(name5, W.fwd_asym(), fl5)
+    for causal in (False, True):
+        nm = "C2_fwd_b2h8s2048d64" + ("_causal" if causal else "")
+        if nm in outputs:
+            fwd(nm, W.fwd_d64(causal), W.fwd_flops(2, 2048, 2048, 8, 64, 64, causal))
+    if "C1_kvcache_empty" in outputs:
+        c1 = W.kvcache_empty()
+        kv("C1_kvcache_empty", c1, None, 0)
+    if "C3_decode_gqa" in outputs:
+        c3 = W.decode_gqa()
+        lens = W.seqlens_list(c3.cache_seqlens, 8)
+        kv("C3_decode_gqa", c3, "oracle_kv_gbs", sum(L + 1 for L in lens) * 8 * 256 * 2 / 1e9)
+    if "C4_chunked_prefill" in outputs:
+        c4 = W.chunked_prefill()
+        lens = W.seqlens_list(c4.cache_seqlens, 4)
+        kv("C4_chunked_prefill", c4, "oracle_tflops", 2.0 * 256 * 16 * W.kvcache_pairs(lens, 512, 512, True) / 1e12)
+    h = per[name5]
+    return {"value": fl5 / h["oracle_s"] / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "the whole headline call (causal B=2 H=16 S=4096 Dqk=192 Dv=128), once, fp64 numpy, "
+                      "%.1f s; every other configuration once in per_config" % h["oracle_s"],
+            "per_config": per}
 
 
 if __name__ == "__main__":

@@ -4,8 +4,8 @@ Argument marshalling only: torch tensors are turned into device pointers,
 element strides and the current HIP stream, and handed to the C ABI declared
 in include/attn.h.  Every step of the computation runs in the library's HIP
 kernels; there is no fallback.  If libattn.so is missing, importing this
-package raises ImportError (build it with ``python -m
-exact_attention_qk_amd.build`` or ``__graft_entry__.build()``).
+package raises ImportError (build it with ``python
+exact_attention_qk_amd/build.py`` or ``__graft_entry__.build()``).
 
 Names follow the pages: ``attn_fwd`` (flash_attn_func), ``attn_fwd_kvcache``
 (flash_attn_with_kvcache) and ``rope_apply`` (the non-fused rotary kernel).
@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libattn.so not found at %s: build it first "
-                      "(python -m exact_attention_qk_amd.build)" % LIB_PATH)
+                      "(python exact_attention_qk_amd/build.py)" % LIB_PATH)
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -175,6 +175,50 @@ def _t4(t):
     return Tensor4(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
 
 
+def _expect(t, shape, dtype, name):
+    """Refuse a tensor whose shape or dtype does not match what the call's other
+    arguments imply: a mismatch would make a kernel read or write outside it."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+
+
+def _lse_ok(lse, shape):
+    if lse is None:
+        return
+    if not (lse.dtype == torch.float32 and lse.is_contiguous() and tuple(lse.shape) == tuple(shape)):
+        raise ValueError("lse must be a contiguous float32 tensor of shape %s" % (tuple(shape),))
+
+
+def _tables_ok(cos, sin, dtype, max_rd):
+    """cos/sin tables: [seqlen_ro, rotary_dim/2], the working dtype, contiguous rows
+    of exactly rotary_dim/2 elements (the kernels index row p at p * rotary_dim/2)."""
+    if (cos is None) != (sin is None):
+        raise ValueError("rotary_cos and rotary_sin must both be given or both be None")
+    if cos is None:
+        return
+    for name, t in (("rotary_cos", cos), ("rotary_sin", sin)):
+        if t.dim() != 2 or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous [seqlen_ro, rotary_dim/2] tensor" % name)
+        if t.dtype != dtype:
+            raise ValueError("%s has dtype %s, expected the working dtype %s" % (name, t.dtype, dtype))
+    if tuple(cos.shape) != tuple(sin.shape):
+        raise ValueError("rotary_cos %s and rotary_sin %s differ in shape" % (tuple(cos.shape), tuple(sin.shape)))
+    if 2 * cos.shape[1] > max_rd:
+        raise ValueError("rotary width 2*%d exceeds head_dim %d" % (cos.shape[1], max_rd))
+
+
+def _offsets_ok(t, B, name):
+    if isinstance(t, torch.Tensor):
+        if not (t.dtype == torch.int32 and t.is_contiguous() and t.dim() == 1):
+            raise ValueError("%s must be an int or a contiguous 1-d int32 tensor" % name)
+        if t.numel() < B:
+            raise ValueError("%s has %d entries for %d batch elements" % (name, t.numel(), B))
+
+
 def _dtype(t):
     if t.dtype not in _DT:
         raise AttnError(-3, "dtype %s is not float16 or bfloat16" % t.dtype)
@@ -192,8 +236,15 @@ def _stream(t):
 # ---------------------------------------------------------------- attn_fwd
 
 def fwd_params(q, k, v, out, causal=False, softmax_scale=None, lse=None, window_size=(-1, -1)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.dim() != 4:
+            raise ValueError("%s must be a [batch, seqlen, heads, head_dim] tensor" % name)
     B, Sq, Hq, Dqk = q.shape
     Sk, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    _expect(k, (B, Sk, Hkv, Dqk), q.dtype, "k")
+    _expect(v, (B, Sk, Hkv, Dv), q.dtype, "v")
+    _expect(out, (B, Sq, Hq, Dv), q.dtype, "out")
+    _lse_ok(lse, (B, Hq, Sq))
     return FwdParams(_dtype(q), B, Sq, Sk, Hq, Hkv, Dqk, Dv, _t4(q), _t4(k), _t4(v), _t4(out),
                      lse.data_ptr() if lse is not None else None, int(bool(causal)),
                      _scale(softmax_scale), int(window_size[0]), int(window_size[1]))
@@ -220,9 +271,19 @@ def attn_fwd(q, k, v, causal=False, softmax_scale=None, out=None, return_lse=Fal
 
 def bwd_params(q, k, v, out, dout, lse, dq, dk, dv, causal=False, softmax_scale=None,
                window_size=(-1, -1)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if t.dim() != 4:
+            raise ValueError("%s must be a [batch, seqlen, heads, head_dim] tensor" % name)
     B, Sq, Hq, Dqk = q.shape
     Sk, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
-    if not (lse.dtype == torch.float32 and lse.is_contiguous() and tuple(lse.shape) == (B, Hq, Sq)):
+    _expect(k, (B, Sk, Hkv, Dqk), q.dtype, "k")
+    _expect(v, (B, Sk, Hkv, Dv), q.dtype, "v")
+    _expect(out, (B, Sq, Hq, Dv), q.dtype, "out")
+    _expect(dout, (B, Sq, Hq, Dv), q.dtype, "dout")
+    _expect(dq, (B, Sq, Hq, Dqk), q.dtype, "dq")
+    _expect(dk, (B, Sk, Hkv, Dqk), q.dtype, "dk")
+    _expect(dv, (B, Sk, Hkv, Dv), q.dtype, "dv")
+    if lse is None or not (lse.dtype == torch.float32 and lse.is_contiguous() and tuple(lse.shape) == (B, Hq, Sq)):
         raise ValueError("lse must be a contiguous float32 [B, Hq, Sq] tensor from the forward call")
     return BwdParams(_dtype(q), B, Sq, Sk, Hq, Hkv, Dqk, Dv, _t4(q), _t4(k), _t4(v), _t4(out), _t4(dout),
                      _t4(dq), _t4(dk), _t4(dv), lse.data_ptr(), int(bool(causal)), _scale(softmax_scale),
@@ -275,8 +336,15 @@ def _codes(t):
 def fp8_params(q, k, v, out, causal=False, softmax_scale=None, lse=None, window_size=(-1, -1),
                descale_q=1.0, descale_k=1.0, descale_v=1.0):
     q, k, v = _codes(q), _codes(k), _codes(v)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.dim() != 4:
+            raise ValueError("%s must be a [batch, seqlen, heads, head_dim] tensor" % name)
     B, Sq, Hq, D = q.shape
     Sk, Hkv = k.shape[1], k.shape[2]
+    _expect(k, (B, Sk, Hkv, D), None, "k")
+    _expect(v, (B, Sk, Hkv, D), None, "v")
+    _expect(out, (B, Sq, Hq, D), torch.bfloat16, "out")
+    _lse_ok(lse, (B, Hq, Sq))
     return Fp8Params(B, Sq, Sk, Hq, Hkv, D, _t4(q), _t4(k), _t4(v), _t4(out),
                      lse.data_ptr() if lse is not None else None, int(bool(causal)), _scale(softmax_scale),
                      float(descale_q), float(descale_k), float(descale_v),
@@ -329,11 +397,20 @@ def _t3(x):
 
 def varlen_params(q, k, v, out, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal=False,
                   softmax_scale=None, lse=None, window_size=(-1, -1)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.dim() != 3:
+            raise ValueError("%s must be a packed [total, heads, head_dim] tensor" % name)
     total_q, Hq, Dqk = q.shape
     total_k, Hkv, Dv = k.shape[0], k.shape[1], v.shape[2]
+    _expect(k, (total_k, Hkv, Dqk), q.dtype, "k")
+    _expect(v, (total_k, Hkv, Dv), q.dtype, "v")
+    _expect(out, (total_q, Hq, Dv), q.dtype, "out")
+    _lse_ok(lse, (Hq, total_q))
     for cu in (cu_seqlens_q, cu_seqlens_k):
-        if not (cu.dtype == torch.int32 and cu.is_contiguous() and cu.is_cuda == q.is_cuda):
-            raise ValueError("cu_seqlens must be contiguous int32 tensors on q's device")
+        if not (cu.dtype == torch.int32 and cu.is_contiguous() and cu.dim() == 1 and cu.is_cuda == q.is_cuda):
+            raise ValueError("cu_seqlens must be contiguous 1-d int32 tensors on q's device")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 offsets")
     B = cu_seqlens_q.numel() - 1
     return VarlenParams(_dtype(q), B, total_q, total_k, int(max_seqlen_q), Hq, Hkv, Dqk, Dv,
                         _t3(q), _t3(k), _t3(v), _t3(out), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
@@ -371,12 +448,23 @@ def prepare_varlen(q, k, v, out, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causa
 def kvcache_params(q, k_cache, v_cache, k=None, v=None, rotary_cos=None, rotary_sin=None,
                    cache_seqlens=0, causal=False, softmax_scale=None, rotary_interleaved=False,
                    out=None, lse=None, workspace=None, num_splits=0, window_size=(-1, -1)):
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("k", k), ("v", v), ("out", out)):
+        if t is not None and t.dim() != 4:
+            raise ValueError("%s must be a [batch, seqlen, heads, head_dim] tensor" % name)
+    if (k is None) != (v is None):
+        raise ValueError("k and v (the new rows) must both be given or both be None")
     B, Sq, Hq, Dqk = q.shape
     cap, Hkv, Dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
     snew = 0 if k is None else k.shape[1]
+    _expect(k_cache, (B, cap, Hkv, Dqk), q.dtype, "k_cache")
+    _expect(v_cache, (B, cap, Hkv, Dv), q.dtype, "v_cache")
+    _expect(k, (B, snew, Hkv, Dqk), q.dtype, "k")
+    _expect(v, (B, snew, Hkv, Dv), q.dtype, "v")
+    _expect(out, (B, Sq, Hq, Dv), q.dtype, "out")
+    _lse_ok(lse, (B, Hq, Sq))
+    _tables_ok(rotary_cos, rotary_sin, q.dtype, Dqk)
+    _offsets_ok(cache_seqlens, B, "cache_seqlens")
     if isinstance(cache_seqlens, torch.Tensor):
-        if not (cache_seqlens.dtype == torch.int32 and cache_seqlens.is_contiguous()):
-            raise ValueError("cache_seqlens must be an int or a contiguous int32 tensor")
         cs_scalar, cs_ptr = 0, cache_seqlens.data_ptr()
     else:
         cs_scalar, cs_ptr = int(cache_seqlens), None
@@ -432,10 +520,15 @@ def attn_fwd_kvcache(q, k_cache, v_cache, k=None, v=None, rotary_cos=None, rotar
 # ---------------------------------------------------------------- rope
 
 def rope_params(x, cos, sin, offsets=0, interleaved=False, conjugate=False, out=None):
+    if x.dim() != 4:
+        raise ValueError("x must be a [batch, seqlen, heads, head_dim] tensor")
     B, S, H, D = x.shape
+    _expect(out, (B, S, H, D), x.dtype, "out")
+    if cos is None or sin is None:
+        raise ValueError("rope_apply needs cos and sin tables")
+    _tables_ok(cos, sin, x.dtype, D)
+    _offsets_ok(offsets, B, "offsets")
     if isinstance(offsets, torch.Tensor):
-        if not (offsets.dtype == torch.int32 and offsets.is_contiguous()):
-            raise ValueError("offsets must be an int or a contiguous int32 tensor")
         off_s, off_p = 0, offsets.data_ptr()
     else:
         off_s, off_p = int(offsets), None

@@ -47,8 +47,14 @@ int check_dtype(attn_dtype d) {
 // (buffer resources and LDS-DMA offsets): 64 rows * 2 bytes * stride < 2^31.
 constexpr int64_t kMaxRowStride = (int64_t)1 << 24;
 
-int check_tensor(const attn_tensor4& t, const char* name) {
+// rows: the tensor's sequence length.  A zero sequence stride over more than
+// one row (an expanded view) is refused: key tiles are read through buffer
+// resources sized rows * stride, which would be empty.
+int check_tensor(const attn_tensor4& t, const char* name, int64_t rows) {
   if (!t.data) return fail(ATTN_E_NULL, "%s: data pointer is NULL", name);
+  if (rows > 1 && t.stride_s == 0)
+    return fail(ATTN_E_UNSUPPORTED, "%s: sequence stride 0 over %lld rows (expanded view) is not supported", name,
+                (long long)rows);
   if (reinterpret_cast<uintptr_t>(t.data) % 16)
     return fail(ATTN_E_ALIGN, "%s: data pointer is not 16-byte aligned", name);
   if (t.stride_b % 8 || t.stride_s % 8 || t.stride_h % 8)
@@ -166,12 +172,12 @@ int validate_fwd(const attn_fwd_params* p) {
   if (p->window_left < -1 || p->window_right < -1)
     return fail(ATTN_E_SHAPE, "window (%d, %d): each side must be >= -1", p->window_left, p->window_right);
   if (p->B == 0 || p->Sq == 0) return ok();
-  if ((e = check_tensor(p->q, "q"))) return e;
+  if ((e = check_tensor(p->q, "q", p->Sq))) return e;
   if (p->Sk > 0) {
-    if ((e = check_tensor(p->k, "k"))) return e;
-    if ((e = check_tensor(p->v, "v"))) return e;
+    if ((e = check_tensor(p->k, "k", p->Sk))) return e;
+    if ((e = check_tensor(p->v, "v", p->Sk))) return e;
   }
-  if ((e = check_tensor(p->out, "out"))) return e;
+  if ((e = check_tensor(p->out, "out", p->Sq))) return e;
   return ok();
 }
 
@@ -215,13 +221,13 @@ int validate_kvcache(const attn_kvcache_params* p) {
   }
   if (p->num_splits < 0) return fail(ATTN_E_SHAPE, "num_splits must be >= 0");
   if (p->B == 0 || p->Sq == 0) return ok();
-  if ((e = check_tensor(p->q, "q"))) return e;
-  if ((e = check_tensor(p->k_cache, "k_cache"))) return e;
-  if ((e = check_tensor(p->v_cache, "v_cache"))) return e;
-  if ((e = check_tensor(p->out, "out"))) return e;
+  if ((e = check_tensor(p->q, "q", p->Sq))) return e;
+  if ((e = check_tensor(p->k_cache, "k_cache", p->capacity))) return e;
+  if ((e = check_tensor(p->v_cache, "v_cache", p->capacity))) return e;
+  if ((e = check_tensor(p->out, "out", p->Sq))) return e;
   if (p->Snew > 0) {
-    if ((e = check_tensor(p->k_new, "k_new"))) return e;
-    if ((e = check_tensor(p->v_new, "v_new"))) return e;
+    if ((e = check_tensor(p->k_new, "k_new", p->Snew))) return e;
+    if ((e = check_tensor(p->v_new, "v_new", p->Snew))) return e;
   }
   const KVPlan plan = plan_kvcache(p);
   if (plan.total > 0) {
@@ -253,8 +259,8 @@ int validate_rope(const attn_rope_params* p) {
   }
   if ((int64_t)p->B * p->S * p->H == 0) return ok();
   if (p->rotary_dim > 0 && (!p->cos || !p->sin)) return fail(ATTN_E_NULL, "cos/sin table is NULL");
-  if ((e = check_tensor(p->x, "x"))) return e;
-  if ((e = check_tensor(p->out, "out"))) return e;
+  if ((e = check_tensor(p->x, "x", p->S))) return e;
+  if ((e = check_tensor(p->out, "out", p->S))) return e;
   return ok();
 }
 
@@ -286,12 +292,12 @@ int validate_varlen(const attn_varlen_params* p) {
     return fail(ATTN_E_SHAPE, "window (%d, %d): each side must be >= -1", p->window_left, p->window_right);
   if (p->B == 0 || p->total_q == 0) return ok();
   if (!p->cu_seqlens_q || !p->cu_seqlens_k) return fail(ATTN_E_NULL, "cu_seqlens_q / cu_seqlens_k is NULL");
-  if ((e = check_tensor(p->q, "q"))) return e;
+  if ((e = check_tensor(p->q, "q", p->total_q))) return e;
   if (p->total_k > 0) {
-    if ((e = check_tensor(p->k, "k"))) return e;
-    if ((e = check_tensor(p->v, "v"))) return e;
+    if ((e = check_tensor(p->k, "k", p->total_k))) return e;
+    if ((e = check_tensor(p->v, "v", p->total_k))) return e;
   }
-  if ((e = check_tensor(p->out, "out"))) return e;
+  if ((e = check_tensor(p->out, "out", p->total_q))) return e;
   return ok();
 }
 
@@ -314,17 +320,17 @@ int validate_bwd(const attn_bwd_params* p) {
     return fail(ATTN_E_SHAPE, "window (%d, %d): each side must be >= -1", p->window_left, p->window_right);
   if (p->B == 0 || (p->Sq == 0 && p->Sk == 0)) return ok();
   if (p->Sq > 0) {
-    if ((e = check_tensor(p->q, "q"))) return e;
-    if ((e = check_tensor(p->out, "out"))) return e;
-    if ((e = check_tensor(p->dout, "dout"))) return e;
-    if ((e = check_tensor(p->dq, "dq"))) return e;
+    if ((e = check_tensor(p->q, "q", p->Sq))) return e;
+    if ((e = check_tensor(p->out, "out", p->Sq))) return e;
+    if ((e = check_tensor(p->dout, "dout", p->Sq))) return e;
+    if ((e = check_tensor(p->dq, "dq", p->Sq))) return e;
     if (!p->lse) return fail(ATTN_E_NULL, "lse is NULL");
   }
   if (p->Sk > 0) {
-    if ((e = check_tensor(p->k, "k"))) return e;
-    if ((e = check_tensor(p->v, "v"))) return e;
-    if ((e = check_tensor(p->dk, "dk"))) return e;
-    if ((e = check_tensor(p->dv, "dv"))) return e;
+    if ((e = check_tensor(p->k, "k", p->Sk))) return e;
+    if ((e = check_tensor(p->v, "v", p->Sk))) return e;
+    if ((e = check_tensor(p->dk, "dk", p->Sk))) return e;
+    if ((e = check_tensor(p->dv, "dv", p->Sk))) return e;
   }
   const size_t need = align_up((size_t)p->B * p->Hq * p->Sq * 2 * sizeof(float));
   if (p->Sq > 0 && p->Sk > 0) {
@@ -344,8 +350,11 @@ void set_t(uint16_t*& ptr, int64_t& sb, int64_t& ss, int64_t& sh, const attn_ten
   ptr = static_cast<uint16_t*>(t.data); sb = t.stride_b; ss = t.stride_s; sh = t.stride_h;
 }
 
-int check_fp8_tensor(const attn_tensor4& t, const char* name) {
+int check_fp8_tensor(const attn_tensor4& t, const char* name, int64_t rows) {
   if (!t.data) return fail(ATTN_E_NULL, "%s: data pointer is NULL", name);
+  if (rows > 1 && t.stride_s == 0)
+    return fail(ATTN_E_UNSUPPORTED, "%s: sequence stride 0 over %lld rows (expanded view) is not supported", name,
+                (long long)rows);
   if (reinterpret_cast<uintptr_t>(t.data) % 16)
     return fail(ATTN_E_ALIGN, "%s: data pointer is not 16-byte aligned", name);
   if (t.stride_b % 16 || t.stride_s % 16 || t.stride_h % 16)
@@ -380,10 +389,10 @@ int validate_fp8(const attn_fp8_params* p) {
   if (!std::isfinite(p->descale_q) || !std::isfinite(p->descale_k) || !std::isfinite(p->descale_v))
     return fail(ATTN_E_SHAPE, "descale factors must be finite");
   if (p->B == 0 || p->Sq == 0) return ok();
-  if ((e = check_fp8_tensor(p->q, "q"))) return e;
+  if ((e = check_fp8_tensor(p->q, "q", p->Sq))) return e;
   if (p->Sk > 0) {
-    if ((e = check_fp8_tensor(p->k, "k"))) return e;
-    if ((e = check_fp8_tensor(p->v, "v"))) return e;
+    if ((e = check_fp8_tensor(p->k, "k", p->Sk))) return e;
+    if ((e = check_fp8_tensor(p->v, "v", p->Sk))) return e;
     const size_t need = fp8_workspace(p);
     if (!p->workspace || p->workspace_bytes < need)
       return fail(ATTN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -391,7 +400,7 @@ int validate_fp8(const attn_fp8_params* p) {
     if (reinterpret_cast<uintptr_t>(p->workspace) % kAlign)
       return fail(ATTN_E_ALIGN, "workspace must be 256-byte aligned");
   }
-  if ((e = check_tensor(p->out, "out"))) return e;
+  if ((e = check_tensor(p->out, "out", p->Sq))) return e;
   return ok();
 }
 

@@ -297,3 +297,138 @@ def test_kvcache_binding_requires_explicit_interleave_flag():
     cos = torch.zeros(4, 32, dtype=torch.float16)
     with pytest.raises(ValueError):
         E.attn_fwd_kvcache(q, q, q, rotary_cos=cos, rotary_sin=cos)
+
+
+# ---------------------------------------------------------------- binding shape checks
+# A tensor whose shape disagrees with the others would make a kernel read or
+# write outside it (a GPU fault, not an error code): the binding refuses it
+# while building the parameter block, before any pointer reaches the library.
+
+def test_fwd_params_refuse_mismatched_tensors():
+    q, k, v, out = _t((2, 8, 4, 64)), _t((2, 8, 2, 64)), _t((2, 8, 2, 64)), _t((2, 8, 4, 64))
+    E.fwd_params(q, k, v, out)
+    for bad_k in (_t((1, 8, 2, 64)), _t((2, 8, 2, 32)), _t((2, 8, 2, 64), torch.bfloat16)):
+        with pytest.raises(ValueError):
+            E.fwd_params(q, bad_k, v, out)
+    with pytest.raises(ValueError):
+        E.fwd_params(q, k, _t((2, 9, 2, 64)), out)           # v length differs from k
+    with pytest.raises(ValueError):
+        E.fwd_params(q, k, _t((2, 8, 1, 64)), out)           # v heads differ from k
+    with pytest.raises(ValueError):
+        E.fwd_params(q, k, v, _t((2, 8, 4, 32)))             # out head_dim != Dv
+    with pytest.raises(ValueError):
+        E.fwd_params(q, k, v, out, lse=torch.zeros(2, 4, 7))  # lse shape
+    with pytest.raises(ValueError):
+        E.fwd_params(q, k, v, out, lse=torch.zeros(2, 4, 8, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        E.fwd_params(q[0], k, v, out)                        # not 4-d
+
+
+def test_bwd_params_refuse_mismatched_tensors():
+    q, k = _t((2, 8, 4, 64)), _t((2, 8, 2, 64))
+    lse = torch.zeros(2, 4, 8)
+    E.bwd_params(q, k, k, q, q, lse, q, k, k)
+    with pytest.raises(ValueError):
+        E.bwd_params(q, k, k, q, _t((2, 7, 4, 64)), lse, q, k, k)     # dout
+    with pytest.raises(ValueError):
+        E.bwd_params(q, k, k, q, q, lse, _t((2, 8, 4, 32)), k, k)     # dq
+    with pytest.raises(ValueError):
+        E.bwd_params(q, k, k, q, q, lse, q, _t((2, 8, 4, 64)), k)     # dk heads
+    with pytest.raises(ValueError):
+        E.bwd_params(q, k, k, q, q, lse, q, k, _t((2, 9, 2, 64)))     # dv length
+    with pytest.raises(ValueError):
+        E.bwd_params(q, k, k, q, q, torch.zeros(2, 4, 9), q, k, k)    # lse
+
+
+def test_fp8_params_refuse_mismatched_tensors():
+    q8 = torch.zeros(2, 8, 4, 64, dtype=torch.uint8)
+    k8 = torch.zeros(2, 8, 2, 64, dtype=torch.uint8)
+    out = _t((2, 8, 4, 64), torch.bfloat16)
+    E.fp8_params(q8, k8, k8, out)
+    with pytest.raises(ValueError):
+        E.fp8_params(q8, k8, torch.zeros(2, 6, 2, 64, dtype=torch.uint8), out)
+    with pytest.raises(ValueError):
+        E.fp8_params(q8, k8, k8, _t((2, 8, 4, 64)))          # output must be bf16
+    with pytest.raises(ValueError):
+        E.fp8_params(q8, k8, k8, _t((2, 8, 2, 64), torch.bfloat16))
+
+
+def test_varlen_params_refuse_mismatched_tensors():
+    q, k, out = _t((10, 4, 64)), _t((12, 2, 64)), _t((10, 4, 64))
+    cu = torch.zeros(3, dtype=torch.int32)
+    E.varlen_params(q, k, k, out, cu, cu, 8)
+    with pytest.raises(ValueError):
+        E.varlen_params(q, k, _t((11, 2, 64)), out, cu, cu, 8)
+    with pytest.raises(ValueError):
+        E.varlen_params(q, k, k, _t((10, 4, 32)), cu, cu, 8)
+    with pytest.raises(ValueError):
+        E.varlen_params(q, k, k, out, cu, torch.zeros(4, dtype=torch.int32), 8)
+    with pytest.raises(ValueError):
+        E.varlen_params(q, k, k, out, cu, cu, 8, lse=torch.zeros(4, 9))
+
+
+def test_kvcache_params_refuse_mismatched_tensors():
+    B, cap, D = 2, 64, 128
+    q = _t((B, 1, 8, D), torch.bfloat16)
+    kc = _t((B, cap, 2, D), torch.bfloat16)
+    kn = _t((B, 1, 2, D), torch.bfloat16)
+    out = _t((B, 1, 8, D), torch.bfloat16)
+    cs = torch.zeros(B, dtype=torch.int32)
+    cos = _t((cap, 64), torch.bfloat16)
+    E.kvcache_params(q, kc, kc, kn, kn, cos, cos, cs, True, None, False, out)
+    bad = [
+        dict(v_cache=_t((B, cap - 1, 2, D), torch.bfloat16)),     # capacities differ
+        dict(v_cache=_t((B, cap, 1, D), torch.bfloat16)),         # kv heads differ
+        dict(k=_t((B, 2, 2, D), torch.bfloat16)),                 # k_new / v_new lengths differ
+        dict(v=_t((B, 1, 2, 64), torch.bfloat16)),                # v_new head_dim != Dv
+        dict(out=_t((B, 1, 8, 64), torch.bfloat16)),
+        dict(k_cache=_t((B, cap, 2, D), torch.float16)),          # dtype differs from q
+        dict(cache_seqlens=torch.zeros(B - 1, dtype=torch.int32)),
+        dict(cache_seqlens=torch.zeros(B, dtype=torch.int64)),
+        dict(rotary_cos=_t((cap, 64)), rotary_sin=_t((cap, 64))),  # fp32 tables
+        dict(rotary_cos=_t((cap, 128), torch.bfloat16)[:, :64],    # sliced (strided) table rows
+             rotary_sin=_t((cap, 128), torch.bfloat16)[:, :64]),
+        dict(rotary_sin=_t((cap, 32), torch.bfloat16)),           # cos and sin differ
+        dict(rotary_cos=_t((cap, 72), torch.bfloat16), rotary_sin=_t((cap, 72), torch.bfloat16)),  # 144 > D
+        dict(v=None),                                             # k without v
+    ]
+    for kw in bad:
+        args = dict(q=q, k_cache=kc, v_cache=kc, k=kn, v=kn, rotary_cos=cos, rotary_sin=cos,
+                    cache_seqlens=cs, causal=True, softmax_scale=None, rotary_interleaved=False, out=out)
+        args.update(kw)
+        with pytest.raises(ValueError):
+            E.kvcache_params(**args)
+
+
+def test_rope_params_refuse_mismatched_tensors():
+    x = _t((2, 5, 3, 64))
+    cos = _t((16, 16))
+    E.rope_params(x, cos, cos, 0, False, False, x)
+    with pytest.raises(ValueError):
+        E.rope_params(x, cos, cos, 0, False, False, _t((2, 5, 3, 32)))
+    with pytest.raises(ValueError):
+        E.rope_params(x, _t((16, 16), torch.bfloat16), _t((16, 16), torch.bfloat16), 0, False, False, x)
+    with pytest.raises(ValueError):
+        E.rope_params(x, cos, _t((16, 8)), 0, False, False, x)
+    with pytest.raises(ValueError):
+        E.rope_params(x, cos, cos, torch.zeros(1, dtype=torch.int32), False, False, x)
+
+
+def test_abi_refuses_zero_sequence_stride():
+    # an expanded view (stride 0 along the sequence) would make the tiled
+    # kernel's K/V buffer resources empty: the library refuses it
+    p, keep = _fwd()
+    p.k.stride_s = 0
+    assert _code_fwd(p) == -3
+    assert b"stride 0" in E.lib().attn_last_error()
+    p, keep = _fwd(Sk=1)
+    p.k.stride_s = p.v.stride_s = 0                  # one row: no stride is ever applied
+    assert _code_fwd(p) == 0
+    p, keep = _kv()
+    p.k_cache.stride_s = 0
+    assert _code_kv(p) == -3
+    x = _t((2, 5, 3, 64))
+    cos = _t((16, 16))
+    pr = E.rope_params(x, cos, cos, 0, False, False, x)
+    pr.x.stride_s = 0
+    assert E.lib().attn_validate_rope(ctypes.byref(pr)) == -3
