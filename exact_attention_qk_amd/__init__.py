@@ -31,6 +31,7 @@ ATTN_OK = 0
 ERRORS = {-1: "ATTN_E_NULL", -2: "ATTN_E_SHAPE", -3: "ATTN_E_UNSUPPORTED", -4: "ATTN_E_ALIGN",
           -5: "ATTN_E_WORKSPACE", -6: "ATTN_E_OVERFLOW", -7: "ATTN_E_HIP"}
 EXPORTED = ["attn_fwd", "attn_fwd_varlen", "attn_fwd_kvcache", "attn_fwd_kvcache_workspace_size",
+            "attn_fwd_kvcache_noalloc",
             "attn_bwd", "attn_bwd_workspace_size", "attn_fwd_fp8", "attn_fwd_fp8_workspace_size",
             "rope_apply", "attn_validate_fwd", "attn_validate_varlen", "attn_validate_kvcache",
             "attn_validate_bwd", "attn_validate_fp8", "attn_validate_rope", "attn_last_error",
@@ -124,6 +125,7 @@ _lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
 _lib.attn_fwd_kvcache.argtypes = [ctypes.POINTER(KVCacheParams), ctypes.c_void_p]
 _lib.attn_fwd_kvcache_workspace_size.argtypes = [ctypes.POINTER(KVCacheParams)]
 _lib.attn_fwd_kvcache_workspace_size.restype = ctypes.c_size_t
+_lib.attn_fwd_kvcache_noalloc.argtypes = [ctypes.POINTER(KVCacheParams), ctypes.c_void_p]
 _lib.rope_apply.argtypes = [ctypes.POINTER(RopeParams), ctypes.c_void_p]
 _lib.attn_validate_fwd.argtypes = [ctypes.POINTER(FwdParams)]
 _lib.attn_validate_kvcache.argtypes = [ctypes.POINTER(KVCacheParams)]
@@ -133,7 +135,7 @@ _lib.attn_validate_fp8.argtypes = [ctypes.POINTER(Fp8Params)]
 _lib.attn_fwd_fp8_workspace_size.argtypes = [ctypes.POINTER(Fp8Params)]
 _lib.attn_fwd_fp8_workspace_size.restype = ctypes.c_size_t
 _lib.attn_last_error.restype = ctypes.c_char_p
-for _n in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_kvcache", "attn_bwd", "attn_fwd_fp8", "rope_apply",
+for _n in ("attn_fwd", "attn_fwd_varlen", "attn_fwd_kvcache", "attn_fwd_kvcache_noalloc", "attn_bwd", "attn_fwd_fp8", "rope_apply",
            "attn_validate_fwd", "attn_validate_varlen", "attn_validate_kvcache", "attn_validate_bwd",
            "attn_validate_fp8", "attn_validate_rope", "attn_abi_version"):
     getattr(_lib, _n).restype = ctypes.c_int
@@ -517,6 +519,23 @@ def attn_fwd_kvcache(q, k_cache, v_cache, k=None, v=None, rotary_cos=None, rotar
     return (out, lse) if return_lse else out
 
 
+def attn_fwd_kvcache_noalloc(q, k_cache, v_cache, k=None, v=None, rotary_cos=None, rotary_sin=None,
+                             cache_seqlens=0, causal=False, softmax_scale=None, rotary_interleaved=None,
+                             num_splits=0, out=None, lse=None, window_size=(-1, -1)):
+    """``attn_fwd_kvcache`` through the entry point that allocates nothing: the
+    library's own 16 MiB device scratch replaces the workspace.  ``out`` (and
+    ``lse`` when wanted) must be given, so this call allocates nothing either."""
+    if rotary_cos is not None and rotary_interleaved is None:
+        raise ValueError("rotary_interleaved must be given explicitly with rotary tables")
+    if out is None:
+        raise ValueError("attn_fwd_kvcache_noalloc needs a preallocated out tensor")
+    p = kvcache_params(q, k_cache, v_cache, k, v, rotary_cos, rotary_sin, cache_seqlens, causal,
+                       softmax_scale, bool(rotary_interleaved), out, lse, None, num_splits, window_size)
+    _on_gpu(q, k_cache, v_cache, k, v, rotary_cos, rotary_sin, cache_seqlens, out, lse)
+    _check(_lib.attn_fwd_kvcache_noalloc(ctypes.byref(p), _stream(q)))
+    return out
+
+
 # ---------------------------------------------------------------- rope
 
 def rope_params(x, cos, sin, offsets=0, interleaved=False, conjugate=False, out=None):
@@ -590,7 +609,7 @@ def prepare_kvcache(q, k_cache, v_cache, k, v, out, *, rotary_cos=None, rotary_s
 
 __all__ = ["PreparedCall", "prepare_fwd", "prepare_varlen", "prepare_kvcache", "prepare_bwd", "attn_bwd",
            "BwdParams", "bwd_params", "attn_fwd", "attn_fwd_varlen",
-           "attn_fwd_kvcache", "rope_apply", "kvcache_workspace_size", "AttnError",
+           "attn_fwd_kvcache", "attn_fwd_kvcache_noalloc", "rope_apply", "kvcache_workspace_size", "AttnError",
            "FwdParams", "VarlenParams", "KVCacheParams", "RopeParams", "Tensor4", "fwd_params",
            "varlen_params", "kvcache_params", "Fp8Params", "fp8_params", "attn_fwd_fp8", "prepare_fp8",
            "rope_params", "lib", "EXPORTED", "LIB_PATH"]

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "attn.h"
@@ -181,7 +182,9 @@ int validate_fwd(const attn_fwd_params* p) {
   return ok();
 }
 
-int validate_kvcache(const attn_kvcache_params* p) {
+// check_ws: whether the caller's workspace is checked (the no-allocation entry
+// point brings its own scratch instead)
+int validate_kvcache(const attn_kvcache_params* p, bool check_ws = true) {
   if (!p) return fail(ATTN_E_NULL, "params pointer is NULL");
   int e;
   if ((e = check_dtype(p->dtype))) return e;
@@ -230,7 +233,7 @@ int validate_kvcache(const attn_kvcache_params* p) {
     if ((e = check_tensor(p->v_new, "v_new", p->Snew))) return e;
   }
   const KVPlan plan = plan_kvcache(p);
-  if (plan.total > 0) {
+  if (check_ws && plan.total > 0) {
     if (!p->workspace)
       return fail(ATTN_E_WORKSPACE, "workspace of %zu bytes required, got NULL", plan.total);
     if (p->workspace_bytes < plan.total)
@@ -560,32 +563,38 @@ size_t attn_fwd_kvcache_workspace_size(const attn_kvcache_params* p) {
   return plan_kvcache(p).total;
 }
 
-int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream) {
-  int e = validate_kvcache(p);
-  if (e) return e;
-  if (p->B == 0 || p->Sq == 0) return ok();
-  hipStream_t st = static_cast<hipStream_t>(stream);
+}  // extern "C"
+
+namespace {
+
+// The kvcache call after validation: ws is the workspace the plan's offsets
+// point into (the caller's, or the no-allocation entry point's scratch).
+int run_kvcache(const attn_kvcache_params* p, hipStream_t st, char* ws) {
   const KVPlan plan = plan_kvcache(p);
   const bool bf16 = p->dtype == ATTN_DTYPE_BF16;
   const int maxrows = p->Sq > p->Snew ? p->Sq : p->Snew;
 
   if (p->cache_seqlens && env_check()) {
-    std::vector<int32_t> h(p->B);
-    hipError_t he = hipMemcpyAsync(h.data(), p->cache_seqlens, sizeof(int32_t) * p->B,
-                                   hipMemcpyDeviceToHost, st);
-    if (he == hipSuccess) he = hipStreamSynchronize(st);
-    if (he != hipSuccess) return hip_fail(he, "ATTN_CHECK copy of cache_seqlens");
-    for (int b = 0; b < p->B; ++b) {
-      if (h[b] < 0 || (int64_t)h[b] + p->Snew > p->capacity)
-        return fail(ATTN_E_OVERFLOW, "cache_seqlens[%d] = %d with Snew %d does not fit capacity %d", b,
-                    h[b], p->Snew, p->capacity);
-      if (plan.rotary && (int64_t)h[b] + maxrows > p->seqlen_ro)
-        return fail(ATTN_E_SHAPE, "cache_seqlens[%d] = %d: positions exceed the rotary tables (%d rows)",
-                    b, h[b], p->seqlen_ro);
+    // debug mode: copy the device lengths to the host in fixed-size chunks
+    // (no allocation) and validate them before anything is launched
+    int32_t h[256];
+    for (int b0 = 0; b0 < p->B; b0 += 256) {
+      const int n = p->B - b0 < 256 ? p->B - b0 : 256;
+      hipError_t he = hipMemcpyAsync(h, p->cache_seqlens + b0, sizeof(int32_t) * n, hipMemcpyDeviceToHost, st);
+      if (he == hipSuccess) he = hipStreamSynchronize(st);
+      if (he != hipSuccess) return hip_fail(he, "ATTN_CHECK copy of cache_seqlens");
+      for (int i = 0; i < n; ++i) {
+        const int b = b0 + i;
+        if (h[i] < 0 || (int64_t)h[i] + p->Snew > p->capacity)
+          return fail(ATTN_E_OVERFLOW, "cache_seqlens[%d] = %d with Snew %d does not fit capacity %d", b,
+                      h[i], p->Snew, p->capacity);
+        if (plan.rotary && (int64_t)h[i] + maxrows > p->seqlen_ro)
+          return fail(ATTN_E_SHAPE, "cache_seqlens[%d] = %d: positions exceed the rotary tables (%d rows)",
+                      b, h[i], p->seqlen_ro);
+      }
     }
   }
 
-  char* ws = static_cast<char*>(p->workspace);
   uint16_t* qrot = (plan.rotary && !plan.fused && !plan.rotq) ? reinterpret_cast<uint16_t*>(ws + plan.off_qrot)
                                                                : nullptr;
   const int64_t qr_sh = p->Dqk, qr_ss = (int64_t)p->Hq * p->Dqk, qr_sb = (int64_t)p->Sq * qr_ss;
@@ -680,6 +689,66 @@ int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream) {
   }
   if (he != hipSuccess) return hip_fail(he, "kvcache attention launch");
   return ok();
+}
+
+// ---------------------------------------------------------------- no-allocation scratch
+// Device memory for the workspace of attn_fwd_kvcache_noalloc: one array per
+// GPU the library runs on, held until the process ends.  Its device address
+// is looked up once per device (with that device current) and kept; host code
+// never hands the array's own name to a kernel.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The scratch address on the device that runs `st` (ATTN_OK), or an error code.
+int scratch_for(hipStream_t st, char** out) {
+  int cur = 0;
+  hipError_t he = hipGetDevice(&cur);
+  if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
+  int dev = cur;
+  if (st && (he = hipStreamGetDevice(st, &dev)) != hipSuccess) return hip_fail(he, "hipStreamGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ATTN_E_UNSUPPORTED, "device %d is beyond the %d devices the scratch table holds", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (he = hipSetDevice(dev)) != hipSuccess) return hip_fail(he, "hipSetDevice");
+    void* ptr = nullptr;
+    he = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) hipSetDevice(cur);
+    if (he != hipSuccess) return hip_fail(he, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(ATTN_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream) {
+  int e = validate_kvcache(p);
+  if (e) return e;
+  if (p->B == 0 || p->Sq == 0) return ok();
+  return run_kvcache(p, static_cast<hipStream_t>(stream), static_cast<char*>(p->workspace));
+}
+
+int attn_fwd_kvcache_noalloc(const attn_kvcache_params* p, void* stream) {
+  int e = validate_kvcache(p, false);
+  if (e) return e;
+  if (p->B == 0 || p->Sq == 0) return ok();
+  const KVPlan plan = plan_kvcache(p);
+  if (plan.total > kScratchBytes)
+    return fail(ATTN_E_WORKSPACE,
+                "attn_fwd_kvcache_noalloc: this call needs %zu bytes of workspace, above the %zu-byte device "
+                "scratch; use attn_fwd_kvcache with a caller workspace", plan.total, kScratchBytes);
+  char* ws = nullptr;
+  if (plan.total > 0 && (e = scratch_for(static_cast<hipStream_t>(stream), &ws))) return e;
+  return run_kvcache(p, static_cast<hipStream_t>(stream), ws);
 }
 
 int rope_apply(const attn_rope_params* p, void* stream) {

@@ -213,6 +213,25 @@ typedef struct attn_kvcache_params {
 size_t attn_fwd_kvcache_workspace_size(const attn_kvcache_params* p);
 int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream);
 
+/* ------------------------------------------------ attn_fwd_kvcache_noalloc
+ * For callers that cannot allocate device memory at call time (work under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * attn_fwd_kvcache with the same arguments, results and errors, except that
+ * p->workspace and p->workspace_bytes are ignored.  The workspace comes from
+ * a device array inside the library instead, 16 MiB per GPU, which each GPU
+ * the library runs on holds from its first use until the process ends; its
+ * address is looked up once per device on the first call there.  A call
+ * whose attn_fwd_kvcache_workspace_size() exceeds 16 MiB returns
+ * ATTN_E_WORKSPACE before anything is enqueued (the single-token decode of
+ * B=8, Hkv=8, a 8192-row cache needs 2.1 MiB).  The call allocates nothing:
+ * no hipMalloc/hipFree, no host allocation.  Nothing in the array has to
+ * start at zero: every byte a call reads was written earlier in that call.
+ * Every call on one GPU shares its array, so calls that may overlap on one
+ * GPU (different streams, or host threads without ordering between them)
+ * race: order them on one stream.
+ */
+int attn_fwd_kvcache_noalloc(const attn_kvcache_params* p, void* stream);
+
 /* ------------------------------------------------------------- attn_fwd_fp8
  * attn_fwd on FP8 inputs: the skill page "Flash Attention - Fast
  * Memory-Efficient Attention", Workflow 3 (H100 FP8 optimization with
