@@ -14,7 +14,9 @@ timing together with each configuration's error against it.
 
 GPU time comes from HIP events recorded on the stream the library launches
 on (torch's current stream), around back-to-back calls, with inputs already
-resident in HBM.  The headline, decode and chunked-prefill calls cycle through
+resident in HBM.  Each timed loop is preceded by 50 ms of the same calls,
+untimed (the engine clock ramps up over the first ~10 ms of load), and then
+by the requested warmup calls.  The headline, decode and chunked-prefill calls cycle through
 input replicas (2, 4 and 4) whose total exceeds the 256 MB Infinity Cache, so
 each call reads HBM rather than that cache.
 """
@@ -98,10 +100,22 @@ def peaks():
 
 # ---------------------------------------------------------------- timing
 
+CLOCK_WARMUP_S = 0.05   # untimed calls before each timed loop: the engine clock ramps up over ~10 ms of load
+
+
 def time_loop(calls, steps, warmup, torch):
     """Average seconds per call over `steps` back-to-back calls (cycling through `calls`),
-    from HIP events on the stream the calls enqueue on."""
+    from HIP events on the stream the calls enqueue on.  Before the `warmup` calls, the
+    same calls run untimed for CLOCK_WARMUP_S so that the device is at its working clock."""
     n = len(calls)
+    t0, i = time.perf_counter(), 0
+    while True:
+        calls[i % n]()
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= CLOCK_WARMUP_S:
+                break
     for i in range(warmup):
         calls[i % n]()
     torch.cuda.synchronize()
@@ -237,25 +251,6 @@ def main():
 
     def want(name):
         return not only or name in only   # "none" matches nothing
-
-    # ---------------- C5 (headline): causal B=2 H=16 S=4096 Dqk=192 Dv=128 bf16, 2 replicas
-    c = W.fwd_asym()
-    calls, outs = [], []
-    for r in range(2):
-        q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
-        out = torch.empty((2, 4096, 16, 128), dtype=q.dtype, device=dev)
-        calls.append(E.prepare_fwd(q, k, v, out, True, c.softmax_scale))
-        outs.append(out)
-    t5 = time_loop(calls, K, Wm, torch)
-    t5_one = time_loop(calls[:1], K, Wm, torch)
-    fl5 = W.fwd_flops(2, 4096, 4096, 16, 192, 128, True)
-    name5 = "C5_fwd_asym_b2h16s4096_causal"
-    configs[name5] = {"us": t5 * 1e6, "us_same_inputs": t5_one * 1e6, "gflop": fl5 / 1e9,
-                      "tflops": fl5 / t5 / 1e12, "pct_mfma_peak": 100 * fl5 / t5 / 1e12 / pk["mfma_bf16_tflops"],
-                      "roofline": mfma_entry(name5, fl5, t5, pk, "tile_attn_kernel<BF16,192,128,causal>")}
-    outputs[name5] = outs[0].cpu()
-    del calls, outs, q, k, v, out
-    torch.cuda.empty_cache()
 
     # ---------------- C1: empty-cache kvcache (latency only)
     if want("c1"):
@@ -404,6 +399,27 @@ def main():
                 "peak_note": "Q K^T on fp8 MFMA, P V on bf16 MFMA: blended peak %.0f TFLOP/s" % blend}
             del call, q, k, v, out, c
 
+    # ---------------- C5 (headline): causal B=2 H=16 S=4096 Dqk=192 Dv=128 bf16, 2 replicas.
+    # Timed after the other configurations, so that the device runs at its
+    # working clocks (the first milliseconds of a process run slower).
+    c = W.fwd_asym()
+    calls, outs = [], []
+    for r in range(2):
+        q, k, v = c.q.to(dev), c.k.to(dev), c.v.to(dev)
+        out = torch.empty((2, 4096, 16, 128), dtype=q.dtype, device=dev)
+        calls.append(E.prepare_fwd(q, k, v, out, True, c.softmax_scale))
+        outs.append(out)
+    t5_one = time_loop(calls[:1], K, Wm, torch)
+    t5 = time_loop(calls, K, Wm, torch)
+    fl5 = W.fwd_flops(2, 4096, 4096, 16, 192, 128, True)
+    name5 = "C5_fwd_asym_b2h16s4096_causal"
+    configs[name5] = {"us": t5 * 1e6, "us_same_inputs": t5_one * 1e6, "gflop": fl5 / 1e9,
+                      "tflops": fl5 / t5 / 1e12, "pct_mfma_peak": 100 * fl5 / t5 / 1e12 / pk["mfma_bf16_tflops"],
+                      "roofline": mfma_entry(name5, fl5, t5, pk, "tile_attn_kernel<BF16,192,128,causal>")}
+    outputs[name5] = outs[0].cpu()
+    del calls, outs, q, k, v, out
+    torch.cuda.empty_cache()
+
     if args.copy_mib:
         src = torch.empty(args.copy_mib * 2**20 // 2, dtype=torch.bfloat16, device=dev)
         dst = torch.empty_like(src)
@@ -426,6 +442,7 @@ def main():
                    "global_batch": 2, "seq_len": 4096, "heads": 16, "head_dim_qk": 192, "head_dim_v": 128,
                    "parallelism": "single-gpu"},
         "pct_mfma_peak": h["pct_mfma_peak"],
+        "clock_warmup_s": CLOCK_WARMUP_S,
         "roofline": dict(h["roofline"], algorithmic="2*(192+128) flop x 2*16*4096*4097/2 unmasked (query,key) "
                                                     "pairs = %.5g GFLOP per launch" % (fl5 / 1e9)),
         "decode": configs.get("C3_decode_gqa"),

@@ -26,6 +26,7 @@ struct AttnArgs {
                               // (kNoWindow when a side is unbounded)
   int num_qtiles;             // tiled kernel: ceil(Sq / rows per workgroup)
   int xcd_remap;              // tiled kernel: 1 when the grid is a multiple of 8
+  int lpt;                    // tiled kernel: longest-first unit order from the device-side lengths
   float c;                    // softmax_scale * log2(e)
   float oscale;               // FP8 inputs: the descale of v, applied to the output
   // split-KV decode

@@ -211,5 +211,17 @@ __device__ __forceinline__ int swz_v(int r) {
   else if constexpr (C % 8 == 0) return ((r >> 1) & 3) << 1;
   else return 0;
 }
+// V tiles of the tiled kernel: each 32-lane half of a ds_read_b64_tr_b16
+// reads 4 consecutive rows x 4 adjacent chunks (64 bytes of each row), and
+// the LDS serves 32 lanes (256 bytes, all 64 banks) per cycle for this read.
+// The swizzle moves the 4 rows' chunk quads onto 4 disjoint quarters of the
+// banks: rows of 256 bytes (C = 16) XOR the chunk with 4 * (r % 4); rows of
+// 128 bytes (C = 8, two rows per bank line) with 4 * ((r / 2) % 2).
+template <int C>
+__device__ __forceinline__ int swz_vt(int r) {
+  if constexpr (C % 16 == 0) return (r & 3) << 2;
+  else if constexpr (C % 8 == 0) return ((r >> 1) & 1) << 2;
+  else return 0;
+}
 
 }  // namespace attn

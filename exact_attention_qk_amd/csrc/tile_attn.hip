@@ -53,6 +53,43 @@ __device__ __forceinline__ int key_perm(int m) {
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+// Query rows, key length and query-0 position of batch b (packed sequences,
+// KV cache or plain), and the number of BN-key tiles that query tile qt of
+// BM rows walks under the causal / window bounds.
+struct UnitGeom {
+  int Sqb, qst, kst, L, off;
+};
+__device__ __forceinline__ UnitGeom unit_geom(const AttnArgs& a, int b) {
+  UnitGeom u;
+  u.Sqb = a.Sq; u.qst = 0; u.kst = 0;
+  if (a.varlen) {
+    u.qst = a.cu_q[b];
+    u.Sqb = a.cu_q[b + 1] - u.qst;
+    u.kst = a.cu_k[b];
+    u.L = a.cu_k[b + 1] - u.kst;
+    u.off = u.L - u.Sqb;
+  } else if (a.kvcache) {
+    const int cb = a.seqlens ? a.seqlens[b] : a.seqlen_scalar;
+    u.L = cb + a.Snew;
+    u.off = cb;
+  } else {
+    u.L = a.Sk;
+    u.off = a.Sk - a.Sq;
+  }
+  return u;
+}
+template <bool CAUSAL, bool WIN, int BM, int BN>
+__device__ __forceinline__ int unit_tiles(const AttnArgs& a, const UnitGeom& u, int qt) {
+  const int wrgt = WIN ? (CAUSAL ? min(a.wr, 0) : a.wr) : 0;
+  const int q0 = qt * BM;
+  if (q0 >= u.Sqb) return 0;
+  const int rows_end = min(q0 + BM, u.Sqb);
+  int kend = u.L, kbeg = 0;
+  if (WIN || CAUSAL) kend = max(0, min(u.L, u.off + rows_end + wrgt));
+  if (WIN) kbeg = min(kend, max(0, u.off + q0 - a.wl));
+  return max(0, (kend + BN - 1) / BN - (WIN ? kbeg / BN : 0));
+}
+
 template <class T>
 __device__ __forceinline__ uint32_t pack_p(float a, float b);
 template <>
@@ -112,45 +149,71 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
   const int hh = lane >> 5;
 
   // ---- work unit
-  int u = blockIdx.x;
-  if (a.xcd_remap) {
-    const int per = gridDim.x >> 3;
-    u = (u & 7) * per + (u >> 3);
-  }
-  // PAIR (causal): a unit is the query-tile pair (nqt-1-p, p), processed one
-  // after the other, so every workgroup gets the same number of key tiles.
   const int nqt = a.num_qtiles;
-  const int nub = PAIR ? (nqt + 1) / 2 : nqt;   // units per (batch, head)
-  const int bh = u / nub;
-  const int pu = u - bh * nub;
-  const int b = bh / a.Hq;
-  const int hq = bh - b * a.Hq;
+  int b, hq, pu;
+  if (!PAIR && a.lpt) {
+    // Longest first across batches (per-batch lengths: KV caches, packed
+    // sequences): every workgroup ranks the (batch, query tile) groups by
+    // their key-tile count, computed from the device-side lengths, and takes
+    // the group of its rank.  With Hq a multiple of 8 each XCD owns Hq/8
+    // heads of every group (blockIdx % 8 is the XCD), so a head's K/V stay
+    // in one L2.  The ranking needs B * nqt <= workgroup size (host-checked).
+    const int ng = a.B * nqt;
+    int* rk = reinterpret_cast<int*>(smem);
+    if (tid < ng) rk[tid] = unit_tiles<CAUSAL, WIN, BM, BN>(a, unit_geom(a, tid / nqt), tid % nqt);
+    __syncthreads();
+    int rank, h;
+    const int bid = blockIdx.x;
+    if (a.xcd_remap) {
+      const int hpx = a.Hq >> 3;
+      const int j = bid >> 3;
+      rank = j / hpx;
+      h = (bid & 7) * hpx + (j - rank * hpx);
+    } else {
+      rank = bid / a.Hq;
+      h = bid - rank * a.Hq;
+    }
+    int mine = 0;
+    if (tid < ng) {
+      const int wt = rk[tid];
+      int r = 0;
+      for (int j = 0; j < ng; ++j) {
+        const int wj = rk[j];
+        r += (wj > wt || (wj == wt && j < tid)) ? 1 : 0;
+      }
+      mine = (r == rank) ? tid + 1 : 0;
+    }
+    __syncthreads();
+    if (mine) rk[0] = mine - 1;
+    __syncthreads();
+    const int gsel = min(max(rk[0], 0), ng - 1);   // (exactly one lane matched)
+    __syncthreads();   // the first tile's DMA reuses this LDS
+    b = gsel / nqt;
+    hq = h;
+    pu = gsel - b * nqt;   // the query tile itself (no heavy-first flip below)
+  } else {
+    int u = blockIdx.x;
+    if (a.xcd_remap) {
+      const int per = gridDim.x >> 3;
+      u = (u & 7) * per + (u >> 3);
+    }
+    // PAIR (causal): a unit is the query-tile pair (nqt-1-p, p), processed one
+    // after the other, so every workgroup gets the same number of key tiles.
+    const int nub = PAIR ? (nqt + 1) / 2 : nqt;   // units per (batch, head)
+    const int bh = u / nub;
+    pu = u - bh * nub;
+    b = bh / a.Hq;
+    hq = bh - b * a.Hq;
+  }
   const int hkv = hq / a.group;
   const int nslots = (PAIR && nqt - 1 - pu != pu) ? 2 : 1;
   // packed variable-length batches: sequence b owns query rows [qst, qst + Sqb)
   // and key rows from kst on; the grid covers the longest query sequence
-  int Sqb = a.Sq, qst = 0, kst = 0;
-  if (a.varlen) {
-    qst = a.cu_q[b];
-    Sqb = a.cu_q[b + 1] - qst;
-    kst = a.cu_k[b];
-  }
+  const UnitGeom ug = unit_geom(a, b);
+  const int Sqb = ug.Sqb, qst = ug.qst, kst = ug.kst, L = ug.L, off = ug.off;
   for (int slot = 0; slot < nslots; ++slot) {
   int qt = pu;
-  if (CAUSAL) qt = (PAIR && slot == 1) ? pu : nqt - 1 - pu;   // heavy tiles first
-
-  int L, off;
-  if (a.varlen) {
-    L = a.cu_k[b + 1] - kst;
-    off = L - Sqb;
-  } else if (a.kvcache) {
-    const int cb = a.seqlens ? a.seqlens[b] : a.seqlen_scalar;
-    L = cb + a.Snew;
-    off = cb;
-  } else {
-    L = a.Sk;
-    off = a.Sk - a.Sq;
-  }
+  if (CAUSAL && !a.lpt) qt = (PAIR && slot == 1) ? pu : nqt - 1 - pu;   // heavy tiles first
   // key j is allowed for the query at position p iff p - wlft <= j <= p + wrgt
   // (causal caps wrgt at 0; without a window the bounds are compile-time
   // constants and the unbounded sides drop out)
@@ -201,7 +264,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
   for (int j = 0; j < JV; ++j) {
     const int P = (rw + j * NR) * 64 + lane;
     const int row = P / CV, pos = P % CV;
-    voff_j[j] = row * a.v_ss * 2 + ((pos ^ swz_v<CV>(row)) << 4);
+    voff_j[j] = row * a.v_ss * 2 + ((pos ^ swz_vt<CV>(row)) << 4);
   }
   auto issue = [&](int t, int s) {
     const uint32_t kd = smem_addr + (uint32_t)((g * 2 + s) * STAGE) * 2;
@@ -273,6 +336,34 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
   const int tr_t = (lane & 15) >> 2;
   const int tr_q = lane & 3;
 
+  // LDS read offsets (elements) that depend on the lane only; every other
+  // part of a K or V fragment address is a compile-time constant, so the
+  // reads use instruction offsets instead of per-read address arithmetic.
+  //  * K (S^T = K Q^T): row key_perm(lane) of each 32-key block; the chunk
+  //    swizzle depends on the row modulo 32 only.  When it flips fewer than
+  //    4 chunk bits, chunk 2*st + hh sits at base[st % 4] + 8*(st / 4) chunks.
+  //  * V (O^T += V^T P^T): rows 8*hh + tr_t (+4, +16 t2, +32 kb) share one
+  //    swizzle value; column block i needs its own base.
+  constexpr int NKO = (CK % 16 == 0) ? KSTEPS : (KSTEPS < 4 ? KSTEPS : 4);
+  int koffl[NKO];
+  {
+    const int krow = key_perm(lane & 31);
+    const int sw = swz_k<CK>(krow);
+#pragma unroll
+    for (int j = 0; j < NKO; ++j) koffl[j] = krow * DQK + (((2 * j + hh) ^ sw) << 3);
+  }
+  int voffl[DVB];
+  {
+    const int vrow = 8 * hh + tr_t;
+    const int sv = swz_vt<CV>(vrow);
+#pragma unroll
+    for (int i = 0; i < DVB; ++i) {
+      int col = i * 32 + 16 * (grp & 1) + 4 * tr_q;
+      if (DV < 32 && (grp & 1)) col = 4 * tr_q;   // lanes past a 16-wide V read a valid spot and are zeroed
+      voffl[i] = vrow * DV + (((col >> 3) ^ sv) << 3) + (col & 7);
+    }
+  }
+
   // One key tile per call; the loop makes two calls per trip so that each
   // call's LDS stage is a constant (its addresses become instruction offsets
   // of loop-invariant registers).
@@ -293,8 +384,35 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
     f32x16 sc[RB][NKB];
     bool blk_on[NKB];
 #pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) blk_on[kb] = key0 + kb * 32 < wkend && (!WIN || key0 + kb * 32 + 32 > wkbeg);
+    // K fragment kb, k-step st of this stage (16 bytes per lane)
+    auto kfrag = [&](int kb, int st) -> u32x4 {
+      const int o = (CK % 16 == 0) ? koffl[st] : koffl[st % 4] + 64 * (st / 4);
+      return *reinterpret_cast<const u32x4*>(kt + kb * 32 * DQK + o);
+    };
+    bool all_on = true;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) all_on = all_on && blk_on[kb];
+    bool s_done = false;
+    if constexpr (!F8) {
+      if (all_on) {
+        // every block is in the band (the common case): the blocks' MFMA
+        // chains are independent and interleave
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st)
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            const u32x4 af = kfrag(kb, st);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              sc[rb][kb] = T::mfma32(af, qf[rb][st], st == 0 ? (f32x16){} : sc[rb][kb]);
+          }
+        s_done = true;
+      }
+    }
+    if (!s_done)
+#pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      blk_on[kb] = key0 + kb * 32 < wkend && (!WIN || key0 + kb * 32 + 32 > wkbeg);
       if (blk_on[kb]) {
         const int krow = kb * 32 + key_perm(lane & 31);
         const int sw = swz_k<CK>(krow);
@@ -313,10 +431,9 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
                   af, q8[rb][st], st == 0 ? (f32x16){} : sc[rb][kb], 0, 0, 0, 0, 0, 0);
           }
         } else {
-          const uint16_t* kr = kt + krow * DQK;
 #pragma unroll
           for (int st = 0; st < KSTEPS; ++st) {
-            const u32x4 af = *reinterpret_cast<const u32x4*>(kr + (((2 * st + hh) ^ sw) << 3));
+            const u32x4 af = kfrag(kb, st);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
               sc[rb][kb] = T::mfma32(af, qf[rb][st], st == 0 ? (f32x16){} : sc[rb][kb]);
@@ -397,16 +514,12 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
       if (!blk_on[kb]) continue;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
-        const int rowa = kb * 32 + 16 * t2 + 8 * hh + tr_t;
-        const int rowb = rowa + 4;
 #pragma unroll
         for (int i = 0; i < DVB; ++i) {
-          int col = i * 32 + 16 * (grp & 1) + 4 * tr_q;
           const bool dead = (DV < 32) && (grp & 1);
-          if (dead) col = 4 * tr_q;
-          const int ch = col >> 3, within = col & 7;
-          const u32x2 lo = lds_read_tr16(vt + rowa * DV + ((ch ^ swz_v<CV>(rowa)) << 3) + within);
-          const u32x2 hi = lds_read_tr16(vt + rowb * DV + ((ch ^ swz_v<CV>(rowb)) << 3) + within);
+          const uint16_t* vp = vt + (kb * 32 + 16 * t2) * DV + voffl[i];
+          const u32x2 lo = lds_read_tr16(vp);
+          const u32x2 hi = lds_read_tr16(vp + 4 * DV);
           u32x4 af = (u32x4){lo[0], lo[1], hi[0], hi[1]};
           if (dead) af = (u32x4){0, 0, 0, 0};
 #pragma unroll
@@ -529,7 +642,11 @@ static hipError_t launch_cfg(const AttnArgs& a0, bool fastc, hipStream_t st) {
   a.num_qtiles = (a.Sq + BM - 1) / BM;
   const int64_t units = (int64_t)a.B * a.Hq * (PAIR ? (a.num_qtiles + 1) / 2 : a.num_qtiles);
   if (units <= 0) return hipSuccess;
-  a.xcd_remap = (units % 8 == 0) ? 1 : 0;
+  // longest-first order across batches when their lengths differ (per-batch
+  // cache lengths, packed sequences) and the ranking fits one workgroup
+  a.lpt = (!PAIR && (a.varlen || (a.kvcache && a.seqlens)) &&
+           (int64_t)a.B * a.num_qtiles <= 64 * NR * NS) ? 1 : 0;
+  a.xcd_remap = a.lpt ? (a.Hq % 8 == 0 && units % 8 == 0) : (units % 8 == 0);
   const dim3 grid((unsigned)units), block(64 * NR * NS);
   if (fastc)
     hipLaunchKernelGGL((tile_attn_kernel<T, DQK, DV, CAUSAL, WIN, RB, NR, NS, BN, PAIR, true, MINW, F8, ROTQ>), grid,
@@ -564,12 +681,22 @@ static hipError_t launch_dims(const AttnArgs& a, bool fastc, hipStream_t st) {
     }
     return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 2, 64, false, 2, F8, ROTQ>(a, fastc, st);
   } else {
-    // one query block per wave keeps two waves per SIMD at these head sizes;
+    // one query block per wave keeps two waves per SIMD at these head sizes
+    // (two row blocks per wave need ~300 VGPRs, one wave per SIMD: 1.9x slower
+    // at B2 H16 S4096 D192/128 causal).
+    // causal prefill without a window: complementary query-tile pairs, so that
+    // every workgroup walks the same number of key tiles (measured at B2 H16
+    // S4096 causal: D192/128 197 -> 169 us, D128 167 -> 142 us; the longest-
+    // first order per (batch, head) left a tail of heavy tiles started late)
     // small head-128 problems also split the keys in two, so that a launch of
     // a few hundred workgroups still has two waves per SIMD (measured: D=128
     // B2 H8 S2048 49.8 -> 42.3 us, chunked prefill 66.4 -> 58.4 us)
     if (DQK <= 128 && rows <= 256 * 256)
       return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 2, 64, false, 2, F8, ROTQ>(a, fastc, st);
+    if constexpr (CAUSAL && !WIN) {
+      if (!a.varlen && !a.kvcache)
+        return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 1, 64, true, 2, F8, ROTQ>(a, fastc, st);
+    }
     return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 1, 64, false, 2, F8, ROTQ>(a, fastc, st);
   }
 }
