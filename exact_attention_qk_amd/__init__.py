@@ -355,9 +355,12 @@ def fp8_params(q, k, v, out, causal=False, softmax_scale=None, lse=None, window_
 
 def _fp8_workspace(p, device):
     need = int(_lib.attn_fwd_fp8_workspace_size(ctypes.byref(p)))
+    if need == 0:
+        p.workspace, p.workspace_bytes = None, 0
+        return None
     ws = torch.empty(need + 256, dtype=torch.uint8, device=device)
     off = (-ws.data_ptr()) % 256
-    p.workspace = ws.data_ptr() + off if need else None
+    p.workspace = ws.data_ptr() + off
     p.workspace_bytes = need
     return ws
 

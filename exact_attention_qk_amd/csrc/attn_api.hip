@@ -371,10 +371,8 @@ int check_fp8_tensor(const attn_tensor4& t, const char* name, int64_t rows) {
   return ATTN_OK;
 }
 
-size_t fp8_workspace(const attn_fp8_params* p) {
-  if (!p || p->B < 0 || p->Sk < 0 || p->Hkv < 1 || p->D < 0) return 0;
-  return align_up((size_t)p->B * p->Sk * p->Hkv * p->D * 2);
-}
+// The FP8 path converts v inside the attention kernel: no workspace.
+size_t fp8_workspace(const attn_fp8_params*) { return 0; }
 
 int validate_fp8(const attn_fp8_params* p) {
   if (!p) return fail(ATTN_E_NULL, "params pointer is NULL");
@@ -396,12 +394,6 @@ int validate_fp8(const attn_fp8_params* p) {
   if (p->Sk > 0) {
     if ((e = check_fp8_tensor(p->k, "k", p->Sk))) return e;
     if ((e = check_fp8_tensor(p->v, "v", p->Sk))) return e;
-    const size_t need = fp8_workspace(p);
-    if (!p->workspace || p->workspace_bytes < need)
-      return fail(ATTN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                  p->workspace ? p->workspace_bytes : (size_t)0);
-    if (reinterpret_cast<uintptr_t>(p->workspace) % kAlign)
-      return fail(ATTN_E_ALIGN, "workspace must be 256-byte aligned");
   }
   if ((e = check_tensor(p->out, "out", p->Sq))) return e;
   return ok();
@@ -489,15 +481,7 @@ int attn_fwd_fp8(const attn_fp8_params* p, void* stream) {
   if (p->B == 0 || p->Sq == 0) return ok();
   hipStream_t st = static_cast<hipStream_t>(stream);
   attn::AttnArgs a = base_args();
-  set_q(a, p->q); set_k(a, p->k); set_o(a, p->out);
-  if (p->Sk > 0) {
-    // v as bf16, contiguous [B, Sk, Hkv, D]
-    hipError_t he = attn::run_e4m3_to_bf16(p->v.data, p->v.stride_b, p->v.stride_s, p->v.stride_h, p->workspace,
-                                           p->B, p->Sk, p->Hkv, p->D, st);
-    if (he != hipSuccess) return hip_fail(he, "attn_fwd_fp8 v conversion");
-    a.v = static_cast<const uint16_t*>(p->workspace);
-    a.v_ss = (int64_t)p->Hkv * p->D; a.v_sb = a.v_ss * p->Sk; a.v_sh = p->D;
-  }
+  set_q(a, p->q); set_k(a, p->k); set_v(a, p->v); set_o(a, p->out);   // e4m3 q, k, v: byte strides
   a.lse = p->lse;
   a.lse_sb = (int64_t)p->Hq * p->Sq; a.lse_sh = p->Sq;
   a.B = p->B; a.Sq = p->Sq; a.Sk = p->Sk; a.Hq = p->Hq; a.Hkv = p->Hkv; a.group = p->Hq / p->Hkv;
@@ -717,7 +701,7 @@ int scratch_for(hipStream_t st, char** out) {
     if (dev != cur && (he = hipSetDevice(dev)) != hipSuccess) return hip_fail(he, "hipSetDevice");
     void* ptr = nullptr;
     he = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
-    if (dev != cur) hipSetDevice(cur);
+    if (dev != cur) (void)hipSetDevice(cur);
     if (he != hipSuccess) return hip_fail(he, "hipGetSymbolAddress(scratch)");
     if (!ptr) return fail(ATTN_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
     g_scratch_ptr[dev] = ptr;

@@ -6,11 +6,8 @@
 namespace attn {
 hipError_t run_tile_attn(const AttnArgs& a, int dtype_bf16, int dqk, int dv, bool causal,
                          hipStream_t st);
-// q, k: e4m3 codes (byte strides); v: bf16; output bf16.  d in {64, 128}.
+// q, k, v: e4m3 codes (byte strides); output bf16.  d in {64, 128}.
 hipError_t run_tile_attn_fp8(const AttnArgs& a, int d, bool causal, hipStream_t st);
-// e4m3 [B, S, H, D] (byte strides) -> contiguous bf16 [B, S, H, D]
-hipError_t run_e4m3_to_bf16(const void* src, int64_t sb, int64_t ss, int64_t sh, void* dst, int B, int S, int H,
-                            int D, hipStream_t st);
 hipError_t run_decode_attn(const AttnArgs& a, int dtype_bf16, int dqk, int dv, bool causal,
                            hipStream_t st);
 hipError_t run_rope_rows(const RowSet* sets, int nsets, int dtype_bf16, hipStream_t st);

@@ -243,6 +243,10 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
                          ((int64_t)b * a.k_sb + (int64_t)kst * a.k_ss + (int64_t)hkv * a.k_sh) * EK;
   const int64_t kss = a.k_ss * EK;                       // bytes between key rows
   const uint16_t* vbase = a.v + (int64_t)b * a.v_sb + (int64_t)kst * a.v_ss + (int64_t)hkv * a.v_sh;
+  // F8: v holds e4m3 codes too (strides in bytes); each tile is loaded into
+  // registers, converted exactly to the 16-bit type and written to the V stage
+  const uint8_t* vbase8 = reinterpret_cast<const uint8_t*>(a.v) +
+                          ((int64_t)b * a.v_sb + (int64_t)kst * a.v_ss + (int64_t)hkv * a.v_sh);
 
   // ---- tile DMA: tile t of this group into stage s.  Each lane's source row
   // and chunk inside a tile do not depend on the tile, so their byte offsets
@@ -266,24 +270,65 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
     const int row = P / CV, pos = P % CV;
     voff_j[j] = row * a.v_ss * 2 + ((pos ^ swz_vt<CV>(row)) << 4);
   }
+  // F8 V: lane part of each 16-byte load (global byte offset inside the tile,
+  // and the two LDS chunks its 16 converted elements land in)
+  constexpr int JV8 = F8 ? (BN * DV) / (NR * 64 * 16) : 1;
+  static_assert(!F8 || (BN * DV) % (NR * 64 * 16) == 0, "fp8 V tile split");
+  int v8off[JV8], v8lds0[JV8], v8lds1[JV8];
+  i32x4 v8raw[JV8];
+#pragma unroll
+  for (int j = 0; j < JV8; ++j) {
+    const int P = (rw + j * NR) * 64 + lane;
+    const int row = (P * 16) / DV, c0 = (P * 16) % DV;   // 16 elements: chunks c0/8 and c0/8 + 1
+    v8off[j] = row * (int)a.v_ss + c0;
+    v8lds0[j] = row * DV + (((c0 >> 3) ^ swz_vt<CV>(row)) << 3);
+    v8lds1[j] = row * DV + ((((c0 >> 3) + 1) ^ swz_vt<CV>(row)) << 3);
+  }
   auto issue = [&](int t, int s) {
     const uint32_t kd = smem_addr + (uint32_t)((g * 2 + s) * STAGE) * 2;
     const uint32_t vd = kd + KT * 2;
     const int key0 = t * BN;
     const int rows = min(BN, L - key0);
     const i32x4 rk = make_rsrc(kbase + (int64_t)key0 * kss, rows * kss);
-    const i32x4 rv = make_rsrc(vbase + (int64_t)key0 * a.v_ss, rows * a.v_ss * 2);
 #pragma unroll
     for (int j = 0; j < JK; ++j) {
       const int I = rw + j * NR;
       if (NIK % NR == 0 || I < NIK)
         dma_b128(rk, kd + I * 1024, koff_j[j]);
     }
+    if constexpr (F8) {
+      // rows past the key length read as zero (bounded resource), like the DMA
+      const __amdgpu_buffer_rsrc_t rv8 = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(vbase8 + (int64_t)key0 * a.v_ss), (short)0, rows * (int)a.v_ss, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < JV; ++j) {
-      const int I = rw + j * NR;
-      if (NIV % NR == 0 || I < NIV)
-        dma_b128(rv, vd + I * 1024, voff_j[j]);
+      for (int j = 0; j < JV8; ++j) v8raw[j] = __builtin_amdgcn_raw_buffer_load_b128(rv8, v8off[j], 0, 0);
+    } else {
+      const i32x4 rv = make_rsrc(vbase + (int64_t)key0 * a.v_ss, rows * a.v_ss * 2);
+#pragma unroll
+      for (int j = 0; j < JV; ++j) {
+        const int I = rw + j * NR;
+        if (NIV % NR == 0 || I < NIV)
+          dma_b128(rv, vd + I * 1024, voff_j[j]);
+      }
+    }
+  };
+  // F8: the e4m3 V tile loaded by the last issue() goes to stage s as 16-bit
+  // values (the hardware pair conversion is exact for every code, NaN included)
+  auto v8_store = [&](int s) {
+    if constexpr (F8) {
+      uint16_t* vdst = lds16 + (g * 2 + s) * STAGE + KT;
+#pragma unroll
+      for (int j = 0; j < JV8; ++j) {
+        uint32_t cv[8];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t w = (uint32_t)v8raw[j][d];
+          cv[2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+          cv[2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+        }
+        *reinterpret_cast<u32x4*>(vdst + v8lds0[j]) = (u32x4){cv[0], cv[1], cv[2], cv[3]};
+        *reinterpret_cast<u32x4*>(vdst + v8lds1[j]) = (u32x4){cv[4], cv[5], cv[6], cv[7]};
+      }
     }
   };
 
@@ -372,6 +417,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
     const int tr = it * NS + g;                  // tile index inside the unit
     const int t = t_lo + tr;
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this lane's DMA for stage s landed
+    if (F8 && tr < ntiles) v8_store(s);   // (stage s has been free since the previous barrier)
     __syncthreads();                      // ... and every lane's; stage s^1 is free again
     if (it + 1 < nit && tr + NS < ntiles) issue(t + NS, s ^ 1);
 
@@ -735,53 +781,6 @@ hipError_t run_tile_attn_fp8(const AttnArgs& a, int d, bool causal, hipStream_t 
   if (d == 64) return launch_tile_c<BF16, 64, 64, true>(a, causal, fastc, st);
   if (d == 128) return launch_tile_c<BF16, 128, 128, true>(a, causal, fastc, st);
   return hipErrorInvalidValue;
-}
-
-// One e4m3 code (bits 0..7) as bf16 bits, exactly: normal numbers move their
-// exponent from bias 7 to bias 127 and their 3 mantissa bits to the top of
-// bf16's 7; subnormals m * 2^-9 (m = 1..7) are normal in bf16; S.1111.111 is
-// NaN.  Integer operations only.
-__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
-  const uint32_t sign = (c & 0x80u) << 8, e = (c >> 3) & 0xFu, m = c & 0x7u;
-  uint32_t mag;
-  if (e == 0) {
-    mag = m ? (__builtin_bit_cast(uint32_t, (float)m * 0.001953125f) >> 16) : 0u;   // m * 2^-9
-  } else if (e == 0xFu && m == 0x7u) {
-    mag = 0x7FC0u;
-  } else {
-    mag = ((e + 120u) << 7) | (m << 4);
-  }
-  return sign | mag;
-}
-
-// e4m3 codes -> bf16, [B, S, H, D] with byte strides -> contiguous [B, S, H, D].
-// A lane converts 8 elements.
-__global__ __launch_bounds__(256) void e4m3_to_bf16_kernel(const uint8_t* src, int64_t sb, int64_t ss, int64_t sh,
-                                                           uint16_t* dst, int B, int S, int H, int D) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int CH = D / 8;
-  const int64_t total = (int64_t)B * S * H * CH;
-  if (i >= total) return;
-  const int ch = (int)(i % CH);
-  const int64_t r = i / CH;
-  const int h = (int)(r % H), s = (int)((r / H) % S), b = (int)(r / ((int64_t)H * S));
-  const u32x2 w = *reinterpret_cast<const u32x2*>(src + (int64_t)b * sb + (int64_t)s * ss + (int64_t)h * sh + ch * 8);
-  uint32_t o[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t word = w[j >> 1] >> (16 * (j & 1));
-    o[j] = e4m3_to_bf16_bits(word & 0xFFu) | (e4m3_to_bf16_bits((word >> 8) & 0xFFu) << 16);
-  }
-  stg16(dst + r * D + ch * 8, (u32x4){o[0], o[1], o[2], o[3]});
-}
-
-hipError_t run_e4m3_to_bf16(const void* src, int64_t sb, int64_t ss, int64_t sh, void* dst, int B, int S, int H,
-                            int D, hipStream_t st) {
-  const int64_t total = (int64_t)B * S * H * (D / 8);
-  if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(e4m3_to_bf16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                     static_cast<const uint8_t*>(src), sb, ss, sh, static_cast<uint16_t*>(dst), B, S, H, D);
-  return hipGetLastError();
 }
 
 }  // namespace attn

@@ -249,10 +249,11 @@ int attn_fwd_kvcache_noalloc(const attn_kvcache_params* p, void* stream);
  * D in {64, 128}.  causal, softmax_scale (NaN = 1/sqrt(D)) and the window
  * as in attn_fwd.  descale_*: finite (ATTN_E_SHAPE otherwise).
  * Arithmetic: Q K^T on the fp8 matrix cores with fp32 accumulation (exact
- * products); v is converted to bf16 (exactly) in the workspace; the weights
- * P are rounded to bf16 for the P V product, whose sums are fp32.
- * workspace: attn_fwd_fp8_workspace_size(p) bytes, 256-byte aligned,
- *     scratch (may be NULL when that size is 0).
+ * products); each v tile is converted to bf16 (exactly) as the kernel stages
+ * it in LDS; the weights P are rounded to bf16 for the P V product, whose
+ * sums are fp32.
+ * workspace: attn_fwd_fp8_workspace_size(p) bytes (0: the call needs none;
+ *     workspace may be NULL).  Kept so callers that size one keep working.
  */
 typedef struct attn_fp8_params {
   int B, Sq, Sk, Hq, Hkv, D;

@@ -715,6 +715,23 @@ def test_fp8_strided_views():
     _fp8_check(W.random_fp8(2, 96, 96, 4, 2, 128, False, seed=11), views=True)
 
 
+def test_fp8_every_v_code_is_decoded_exactly():
+    # one key with zero scores: every output row is v itself, so each of the 256
+    # e4m3 codes placed in v must come out as its exact value (times descale_v,
+    # a power of two here), NaN codes as NaN; the codes cover 4 heads x 64 dims
+    from oracle import e4m3_decode
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(1, 1, 4, 64)
+    zero = torch.zeros(1, 1, 4, 64, dtype=torch.uint8)
+    for dv in (1.0, 0.5):
+        out = E().attn_fwd_fp8(dev(zero), dev(zero), dev(codes), descale_v=dv)
+        torch.cuda.synchronize()
+        got = out.float().cpu().double().numpy()
+        ref = e4m3_decode(codes.numpy()) * dv
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan], ref[~nan])
+
+
 def test_fp8_no_keys_gives_zero_rows():
     case = W.random_fp8(1, 5, 0, 2, 2, 64, False, seed=1)
     out, lse = E().attn_fwd_fp8(dev(case.q), dev(case.k), dev(case.v), return_lse=True)
