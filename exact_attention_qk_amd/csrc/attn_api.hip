@@ -135,11 +135,10 @@ KVPlan plan_kvcache(const attn_kvcache_params* p) {
     if (p->num_splits > 0) {
       len = (cap + p->num_splits - 1) / p->num_splits;
     } else {
-      // about 1024 splits when every cache is full (4 per CU on the 256-CU
-      // MI355X): measured fastest for full caches, and within 3 % of the best
-      // for caches filled to half on average; more splits cost partial
-      // writes and merge work, fewer leave CUs idle
-      const double per = (double)cap * p->B * p->Hkv / 1024.0;
+      // about 2048 (kv head, split) waves when every cache is full, 8 per CU
+      // on the 256-CU MI355X (a workgroup holds the waves of up to 8 kv heads
+      // of one split, so a full cache gives about 256 workgroups)
+      const double per = (double)cap * p->B * p->Hkv / 2048.0;
       len = (int)std::ceil(per);
       if (len > 2048) len = 2048;
     }

@@ -153,8 +153,8 @@ __global__ __launch_bounds__(64) void split_merge_kernel(AttnArgs a, int DV) {
   merge_row<T>(a, b, hkv, r, R, nvalid, DV);
 }
 
-template <class T, int DQK, int DV, bool CAUSAL, bool FUSED>
-__global__ __launch_bounds__(64, (DQK > 128 ? 1 : 2)) void decode_attn_kernel(AttnArgs a) {
+template <class T, int DQK, int DV, bool CAUSAL, bool FUSED, int NW>
+__global__ __launch_bounds__(64 * NW, (DQK > 128 ? 1 : 2)) void decode_attn_kernel(AttnArgs a) {
   constexpr int QS = (DQK + 31) / 32;          // 32-dim k-steps of S
   constexpr int CK = DQK / 8;                  // chunks per K row
   constexpr int CV = DV / 8;                   // chunks per V row
@@ -162,25 +162,46 @@ __global__ __launch_bounds__(64, (DQK > 128 ? 1 : 2)) void decode_attn_kernel(At
   constexpr int DVB = DV / 16;                 // 16-wide output blocks
   constexpr int NK = 2 * QS;                   // K loads per lane per step
   static_assert((32 * CV) % 64 == 0, "V step must be whole DMA instructions");
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[3 * 32 * DV];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_all[NW * 2 * 32 * DV];
 
-  const int lane = threadIdx.x;
-  // Workgroup i takes the i-th (batch, split, kv head) that has keys, in that
-  // order, so the busy workgroups are the first ones dispatched and spread
-  // evenly over the CUs whatever the cache lengths; kv heads vary fastest, so
-  // the heads of one split (whose rows share cache lines and DRAM pages) are
-  // fetched at about the same time.  Batches without keys get one workgroup
-  // per kv head (split 0) that writes zeros.
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint16_t* lds_v = lds_all + w * 2 * 32 * DV;   // this wave's two V stages
+  // Workgroup i takes the i-th (batch, split, group of NW kv heads) that has
+  // keys, wave w the group's head w: the NW waves of a workgroup read NW
+  // adjacent head slices of the same cache rows at the same time on one CU
+  // (whole rows when NW = Hkv), which the memory system serves faster than
+  // the same slices fetched from different CUs.  The busy workgroups are
+  // the first ones dispatched, spread evenly over the CUs whatever the cache
+  // lengths.  Batches without keys get one workgroup per head group (split
+  // 0) that writes zeros.
+  const int NG = a.Hkv / NW;
+  // the batch of this workgroup: lanes read 64 batches' lengths at a time and
+  // a wave prefix sum of their workgroup counts finds the batch that holds
+  // item blockIdx.x (one memory round trip instead of one per batch)
   int item = blockIdx.x;
-  int b = 0, nsp_b = 0;
-  for (; b < a.B; ++b) {
-    const SeqInfo sb = seq_info(a, b, CAUSAL);
-    nsp_b = max(1, split_count(a, sb));
-    if (item < nsp_b * a.Hkv) break;
-    item -= nsp_b * a.Hkv;
+  int b = a.B;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int bl = b0 + lane;
+    int cnt = 0;
+    if (bl < a.B) cnt = max(1, split_count(a, seq_info(a, bl, CAUSAL))) * NG;
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(bl < a.B && item < incl);
+    if (hit) {
+      const int first = __builtin_ctzll(hit);
+      b = b0 + first;
+      item -= __shfl(incl - cnt, first);   // workgroups of earlier batches in this chunk
+      break;
+    }
+    item -= __shfl(incl, 63);
   }
   if (b >= a.B) return;   // surplus workgroup
-  const int split = item / a.Hkv, hkv = item - split * a.Hkv;
+  const int split = item / NG, hkv = (item - split * NG) * NW + w;
   const SeqInfo si = seq_info(a, b, CAUSAL);
   const int L = si.L, off = si.off, kend_all = si.kend, wlft = si.wl, wrgt = si.wr;
   const int R = a.group * a.Sq;
@@ -204,20 +225,7 @@ __global__ __launch_bounds__(64, (DQK > 128 ? 1 : 2)) void decode_attn_kernel(At
   const int k_end = min(kend_all, k_begin + a.split_len);
   const int nvalid = split_count(a, si);
 
-  u32x4 qf[QS];
-  {
-    const int tq = min(tok, a.Sq - 1);
-    const uint16_t* qrow = a.q + (int64_t)b * a.q_sb + (int64_t)tq * a.q_ss + (int64_t)min(hq, a.Hq - 1) * a.q_sh;
-#pragma unroll
-    for (int st = 0; st < QS; ++st) {
-      const int d = min(32 * st + 8 * kg, DQK - 8);
-      if (FUSED)
-        qf[st] = rope_chunk<T>(qrow, d, a.rcos, a.rsin, (int64_t)off + tq, a.rd, a.rinter, false);
-      else
-        qf[st] = ldg16(qrow + d);
-      if (!row_ok || 32 * st + 8 * kg >= DQK) qf[st] = (u32x4){0, 0, 0, 0};
-    }
-  }
+  u32x4 qf[QS];   // filled once the first loads are in flight (below)
 
   const uint16_t* kbase = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
   const uint16_t* vbase = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
@@ -230,7 +238,7 @@ __global__ __launch_bounds__(64, (DQK > 128 ? 1 : 2)) void decode_attn_kernel(At
   struct KBuf {
     u32x4 k[2][QS];
   };
-  auto load = [&](int kk, KBuf& B, int stage) {
+  auto load_k = [&](int kk, KBuf& B) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int key = min(kk + 16 * blk + r, k_end - 1);
@@ -240,7 +248,11 @@ __global__ __launch_bounds__(64, (DQK > 128 ? 1 : 2)) void decode_attn_kernel(At
         B.k[blk][st] = ldg16(kbase + (int64_t)key * a.k_ss + d);
       }
     }
+  };
+  auto load_v = [&](int kk, int stage) {
     uint16_t* vd = lds_v + stage * 32 * DV;
+    // the stage's previous contents were read (ds_read) earlier in this wave
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       const int P = j * 64 + lane;
@@ -259,10 +271,12 @@ __global__ __launch_bounds__(64, (DQK > 128 ? 1 : 2)) void decode_attn_kernel(At
   const float c = a.c;
   const int tr_t = (lane & 15) >> 2, tr_q = lane & 3;
 
-  auto step = [&](int kk, const KBuf& B, int stage, int later_steps) {
-    // this step's V DMA has landed once at most the later steps' loads are pending
-    if (later_steps >= 2) VMCNT_WAIT(2 * (NK + VPL));
-    else if (later_steps == 1) VMCNT_WAIT(NK + VPL);
+  // Loads are issued in the order K(i), V(i), K(i+1), V(i+1), ...: step i
+  // waits until at most the next step's loads are pending, and issues the
+  // loads of step i + 2 into its own buffers as soon as it is done with them
+  // (K once the S MFMAs have read it, V once its LDS reads are back).
+  auto step = [&](int kk, KBuf& B, int stage, bool later, bool prefetch) {
+    if (later) VMCNT_WAIT(NK + VPL);
     else VMCNT_WAIT(0);
     const uint16_t* vt = lds_v + stage * 32 * DV;
     f32x4 sa = (f32x4){0, 0, 0, 0}, sb = (f32x4){0, 0, 0, 0};
@@ -273,6 +287,7 @@ __global__ __launch_bounds__(64, (DQK > 128 ? 1 : 2)) void decode_attn_kernel(At
       sa = T::mfma16(ka, qf[st], sa);
       sb = T::mfma16(kb, qf[st], sb);
     }
+    if (prefetch) load_k(kk + 64, B);
     float x[8];
     float mx = -__builtin_inff();
 #pragma unroll
@@ -283,7 +298,7 @@ __global__ __launch_bounds__(64, (DQK > 128 ? 1 : 2)) void decode_attn_kernel(At
       x[i] = ok ? v : -__builtin_inff();
       mx = fmaxf(mx, x[i]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = x16_max(mx);
     mx = xhalf_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const bool grow = m_new > m_run;
@@ -313,6 +328,7 @@ __global__ __launch_bounds__(64, (DQK > 128 ? 1 : 2)) void decode_attn_kernel(At
       const u32x2 hi = lds_read_tr16(vt + rowb * DV + ((ch ^ swz_v<CV>(rowb)) << 3) + within);
       o[i] = T::mfma16((u32x4){lo[0], lo[1], hi[0], hi[1]}, pf, o[i]);
     }
+    if (prefetch) load_v(kk + 64, stage);
   };
 
   // fused append: the split whose range holds positions [c_b, L) first writes
@@ -332,31 +348,43 @@ __global__ __launch_bounds__(64, (DQK > 128 ? 1 : 2)) void decode_attn_kernel(At
         const int key = n0 + id / CV, d = (id % CV) * 8;
         stg16(vc + (int64_t)key * a.v_ss + d, ldg16(vnbase + (int64_t)(key - off) * a.vn_ss + d));
       }
-      __syncthreads();   // stores complete and visible to the whole (single-wave) workgroup
+      __syncthreads();   // stores complete and visible to the workgroup (uniform: one split per workgroup)
     }
   }
 
-  // three-deep pipeline: K registers A/B/C and LDS stages 0/1/2; two steps'
-  // loads are in flight while the current step computes
-  KBuf A, B, C;
-  load(k_begin, A, 0);
-  if (k_begin + 32 < k_end) load(k_begin + 32, B, 1);
+  // two buffers (K registers A/B, LDS stages 0/1) alternate between steps
+  KBuf A, B;
+  load_k(k_begin, A);
+  load_v(k_begin, 0);
+  if (k_begin + 32 < k_end) {
+    load_k(k_begin + 32, B);
+    load_v(k_begin + 32, 1);
+  }
+  // q (rotated at its position when fused), while the first K/V loads are in flight
+  {
+    const int tq = min(tok, a.Sq - 1);
+    const uint16_t* qrow = a.q + (int64_t)b * a.q_sb + (int64_t)tq * a.q_ss + (int64_t)min(hq, a.Hq - 1) * a.q_sh;
+#pragma unroll
+    for (int st = 0; st < QS; ++st) {
+      const int d = min(32 * st + 8 * kg, DQK - 8);
+      if (FUSED)
+        qf[st] = rope_chunk<T>(qrow, d, a.rcos, a.rsin, (int64_t)off + tq, a.rd, a.rinter, false);
+      else
+        qf[st] = ldg16(qrow + d);
+      if (!row_ok || 32 * st + 8 * kg >= DQK) qf[st] = (u32x4){0, 0, 0, 0};
+    }
+  }
+
   for (int kk = k_begin;;) {
-    if (kk + 64 < k_end) load(kk + 64, C, 2);
-    step(kk, A, 0, (kk + 32 < k_end) + (kk + 64 < k_end));
+    step(kk, A, 0, kk + 32 < k_end, kk + 64 < k_end);
     kk += 32;
     if (kk >= k_end) break;
-    if (kk + 64 < k_end) load(kk + 64, A, 0);
-    step(kk, B, 1, (kk + 32 < k_end) + (kk + 64 < k_end));
-    kk += 32;
-    if (kk >= k_end) break;
-    if (kk + 64 < k_end) load(kk + 64, B, 1);
-    step(kk, C, 2, (kk + 32 < k_end) + (kk + 64 < k_end));
+    step(kk, B, 1, kk + 32 < k_end, kk + 64 < k_end);
     kk += 32;
     if (kk >= k_end) break;
   }
 
-  float lt = l_run + __shfl_xor(l_run, 16);
+  float lt = x16_sum(l_run);
   lt = xhalf_sum(lt);
   if (nvalid == 1) {
     // the only split of this (batch, kv head): normalise and store
@@ -387,21 +415,33 @@ __global__ __launch_bounds__(64, (DQK > 128 ? 1 : 2)) void decode_attn_kernel(At
 }
 
 // ---------------------------------------------------------------- launchers
-template <class T, int DQK, int DV>
-static hipError_t launch_decode(const AttnArgs& a, bool causal, hipStream_t st) {
-  const dim3 grid((unsigned)(a.Hkv * a.num_splits * a.B));
+template <class T, int DQK, int DV, int NW>
+static hipError_t launch_decode_nw(const AttnArgs& a, bool causal, hipStream_t st) {
+  const dim3 grid((unsigned)((a.Hkv / NW) * a.num_splits * a.B)), block(64 * NW);
   if (a.fused) {
     if (causal)
-      hipLaunchKernelGGL((decode_attn_kernel<T, DQK, DV, true, true>), grid, dim3(64), 0, st, a);
+      hipLaunchKernelGGL((decode_attn_kernel<T, DQK, DV, true, true, NW>), grid, block, 0, st, a);
     else
-      hipLaunchKernelGGL((decode_attn_kernel<T, DQK, DV, false, true>), grid, dim3(64), 0, st, a);
+      hipLaunchKernelGGL((decode_attn_kernel<T, DQK, DV, false, true, NW>), grid, block, 0, st, a);
   } else {
     if (causal)
-      hipLaunchKernelGGL((decode_attn_kernel<T, DQK, DV, true, false>), grid, dim3(64), 0, st, a);
+      hipLaunchKernelGGL((decode_attn_kernel<T, DQK, DV, true, false, NW>), grid, block, 0, st, a);
     else
-      hipLaunchKernelGGL((decode_attn_kernel<T, DQK, DV, false, false>), grid, dim3(64), 0, st, a);
+      hipLaunchKernelGGL((decode_attn_kernel<T, DQK, DV, false, false, NW>), grid, block, 0, st, a);
   }
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+// Waves per workgroup: the largest of 8, 4, 2, 1 that divides Hkv.
+int decode_waves(int hkv) { return hkv % 8 == 0 ? 8 : hkv % 4 == 0 ? 4 : hkv % 2 == 0 ? 2 : 1; }
+
+template <class T, int DQK, int DV>
+static hipError_t launch_decode(const AttnArgs& a, bool causal, hipStream_t st) {
+  const int nw = decode_waves(a.Hkv);
+  hipError_t e = nw == 8 ? launch_decode_nw<T, DQK, DV, 8>(a, causal, st)
+               : nw == 4 ? launch_decode_nw<T, DQK, DV, 4>(a, causal, st)
+               : nw == 2 ? launch_decode_nw<T, DQK, DV, 2>(a, causal, st)
+                         : launch_decode_nw<T, DQK, DV, 1>(a, causal, st);
   if (e != hipSuccess || a.num_splits <= 1) return e;
   const int64_t rows = (int64_t)a.B * a.Hkv * a.group * a.Sq;
   hipLaunchKernelGGL((split_merge_kernel<T>), dim3((unsigned)rows), dim3(64), 0, st, a, DV);

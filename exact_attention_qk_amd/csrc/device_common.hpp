@@ -107,6 +107,21 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// max / sum of a value held by lane l and lane l^16: v_permlane16_swap(x, x)
+// swaps the odd 16-lane rows of its first operand with the even rows of its
+// second, so its two results are {x[l], x[l+16]} in rows 0 and 2 and
+// {x[l-16], x[l]} in rows 1 and 3 (a VALU exchange, no LDS round trip).
+__device__ __forceinline__ float x16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x), false,
+                                            false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float x16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x), false,
+                                            false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // One rotated 16-bit element: the first member of a pair gives x1*c - x2*s,

@@ -323,6 +323,18 @@ def test_kvcache_decode_many_splits():
     _kv_check(case)
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_kvcache_decode_large_scores(dtype):
+    # q eight times the unit normal: scores of several hundred in log2 units,
+    # so every step's row max must be the true one (a wrong max overflows the
+    # exponentials); 16 query rows per kv head, several splits per row
+    case = W.random_kvcache(2, 1, 16, 1, 128, 128, 1024, dtype, snew=1, seqlens=[1000, 300],
+                            rotary_dim=128, seed=91)
+    case.q = (case.q.float() * 8).to(case.q.dtype)
+    _kv_check(case)
+    _kv_check(case, num_splits=7)
+
+
 def test_kvcache_scalar_and_tensor_seqlens_agree():
     a = W.random_kvcache(2, 1, 4, 1, 128, 128, 512, "bf16", snew=1, seqlens=[300, 300],
                          rotary_dim=128, seed=15)
