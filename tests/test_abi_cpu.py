@@ -246,7 +246,7 @@ def test_kvcache_workspace_plan():
     # rotation happens inside the decode kernel (rd % 16 == 0)
     p, keep = _kv(B=8, Hq=32, Hkv=8, D=128, cap=8192, rotary=128)
     need = E.kvcache_workspace_size(p)
-    split = 8192 * 8 * 8 // 1024          # about 1024 splits when every cache is full
+    split = 8192 * 8 * 8 // 2048          # about 2048 (kv head, split) waves when every cache is full
     nsp = 8192 // split
     R = 4
     cnt = 0
