@@ -109,8 +109,13 @@ struct KVPlan {
   bool fused = false;       // decode kernel also appends the new rows and applies the rotary embedding
   bool rotq = false;        // tiled kernel rotates q as it loads it (the append pass then skips q)
   int split_len = 0, num_splits = 0;
+  int split_auto = 0;       // > 0: the kernels size the splits from the device-side lengths
   size_t off_qrot = 0, off_o = 0, off_ml = 0, total = 0;
 };
+
+// (kv head, split) waves the single-token decode aims for when it sizes its
+// splits from the cache lengths
+constexpr int kSplitWaves = 1408;
 
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
@@ -135,10 +140,14 @@ KVPlan plan_kvcache(const attn_kvcache_params* p) {
     if (p->num_splits > 0) {
       len = (cap + p->num_splits - 1) / p->num_splits;
     } else {
-      // about 2048 (kv head, split) waves when every cache is full, 8 per CU
-      // on the 256-CU MI355X (a workgroup holds the waves of up to 8 kv heads
-      // of one split, so a full cache gives about 256 workgroups)
-      const double per = (double)cap * p->B * p->Hkv / 2048.0;
+      // The kernels pick the split length from the actual key counts, for
+      // about kSplitWaves (kv head, split) waves in all (a workgroup holds the
+      // waves of up to 8 kv heads of one split, so about 176 workgroups on the
+      // 256-CU MI355X; measured on random cache fills, more splits cost more
+      // in the merge than they gain).  The workspace holds splits down to
+      // half the length that full caches would get.
+      k.split_auto = kSplitWaves;
+      const double per = (double)cap * p->B * p->Hkv / (2.0 * kSplitWaves);
       len = (int)std::ceil(per);
       if (len > 2048) len = 2048;
     }
@@ -644,6 +653,7 @@ int run_kvcache(const attn_kvcache_params* p, hipStream_t st, char* ws) {
     a.num_splits = plan.num_splits;
     a.ws_o = reinterpret_cast<float*>(ws + plan.off_o);
     a.ws_ml = reinterpret_cast<float*>(ws + plan.off_ml);
+    a.split_auto = plan.split_auto;
     if (plan.fused) {
       a.fused = 1;
       if (p->Snew > 0) {

@@ -30,7 +30,8 @@ struct AttnArgs {
   float c;                    // softmax_scale * log2(e)
   float oscale;               // FP8 inputs: the descale of v, applied to the output
   // split-KV decode
-  int split_len, num_splits;
+  int split_len, num_splits;   // split length (the smallest one when split_auto), splits per batch at most
+  int split_auto;             // 0, or the number of (kv head, split) waves the kernels size splits for
   float* ws_o;                // [B, Hkv, num_splits, R, Dv] fp32 partial numerators
   float* ws_ml;               // [B, Hkv, num_splits, R, 2]  running max (log2 units), sum
   // decode with the append and the rotary embedding done in the same kernel

@@ -68,15 +68,39 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b, bool causa
   s.kbeg = min(s.kend, max(0, s.off - s.wl));
   return s;
 }
-__device__ __forceinline__ int split_count(const AttnArgs& a, const SeqInfo& s) {
-  return min(a.num_splits, (s.kend - s.kbeg + a.split_len - 1) / a.split_len);
+__device__ __forceinline__ int split_count(const AttnArgs& a, const SeqInfo& s, int split_len) {
+  return min(a.num_splits, (s.kend - s.kbeg + split_len - 1) / split_len);
+}
+
+// Split length: fixed by the host (split_auto == 0), or sized from the
+// actual key counts so that all batches together make about split_auto
+// (kv head, split) waves, never shorter than a.split_len (the length the
+// workspace was sized for).  Every lane of a wave returns the same value.
+__device__ __forceinline__ int split_length(const AttnArgs& a, bool causal) {
+  if (!a.split_auto) return a.split_len;
+  const int lane = threadIdx.x & 63;
+  int tot = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int bl = b0 + lane;
+    int n = 0;
+    if (bl < a.B) {
+      const SeqInfo sb = seq_info(a, bl, causal);
+      n = sb.kend - sb.kbeg;
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) n += __shfl_xor(n, m);
+    tot += n;
+  }
+  const int64_t want = ((int64_t)tot * a.Hkv + a.split_auto - 1) / a.split_auto;
+  return max(a.split_len, (int)((want + 31) / 32 * 32));
 }
 
 // Combine the nvalid splits of query row r of (b, hkv) (one wave).  A lane
-// owns output columns lane and lane + 64.  The partial outputs of the first
-// 32 splits are requested together with the splits' maxima, so the common
-// case needs one round trip to memory; split weights are broadcast with
-// cross-lane reads.
+// owns output columns lane and lane + 64.  Splits are taken 32 at a time: the
+// partial outputs of the chunk and, on lane j, the maximum and sum of its
+// split j are requested together, so a chunk costs one round trip to memory;
+// chunks are combined with a running maximum, and split weights are
+// broadcast with cross-lane reads.
 template <class T>
 __device__ void merge_row(const AttnArgs& a, int b, int hkv, int r, int R, int nvalid, int DV) {
   constexpr int C = 32;
@@ -85,47 +109,34 @@ __device__ void merge_row(const AttnArgs& a, int b, int hkv, int r, int R, int n
   const int tok = r / a.group;
   const int hq = hkv * a.group + (r - tok * a.group);
   const int64_t slot0 = ((int64_t)b * a.Hkv + hkv) * a.num_splits * R + r;
-  auto orow_of = [&](int sp) { return a.ws_o + (slot0 + (int64_t)sp * R) * DV; };
-  float v0[C], v1[C];
+  float M = -__builtin_inff(), lpart = 0.f, acc0 = 0.f, acc1 = 0.f;
+  for (int s0 = 0; s0 < nvalid; s0 += C) {
+    const int n = min(C, nvalid - s0);
+    float v0[C], v1[C];
 #pragma unroll
-  for (int j = 0; j < C; ++j) {
-    const float* os = orow_of(min(j, nvalid - 1));
-    v0[j] = os[dv0];
-    v1[j] = os[dv1];
-  }
-  float M = -__builtin_inff();
-  for (int sp = lane; sp < nvalid; sp += 64) M = fmaxf(M, a.ws_ml[(slot0 + (int64_t)sp * R) * 2]);
-  M = wave_max(M);
-  const float Ms = (M == -__builtin_inff()) ? 0.f : M;
-  float lpart = 0.f, acc0 = 0.f, acc1 = 0.f;
-  for (int s0 = 0; s0 < nvalid; s0 += 64) {
-    // weight of split s0 + lane
-    const int sp = s0 + lane;
-    float w = 0.f;
-    if (sp < nvalid) {
-      const float ms = a.ws_ml[(slot0 + (int64_t)sp * R) * 2];
-      w = (ms == -__builtin_inff()) ? 0.f : fast_exp2(ms - Ms);
-      lpart += w * a.ws_ml[(slot0 + (int64_t)sp * R) * 2 + 1];
+    for (int j = 0; j < C; ++j) {
+      const float* os = a.ws_o + (slot0 + (int64_t)(s0 + min(j, n - 1)) * R) * DV;
+      v0[j] = os[dv0];
+      v1[j] = os[dv1];
     }
-    const int n = min(64, nvalid - s0);
-    for (int j0 = 0; j0 < n; j0 += C) {
-      if (s0 + j0 > 0) {
+    const float* ml = a.ws_ml + (slot0 + (int64_t)(s0 + min(lane, n - 1)) * R) * 2;
+    const float ms = lane < n ? ml[0] : -__builtin_inff();
+    const float ls = lane < n ? ml[1] : 0.f;
+    const float Mn = fmaxf(M, wave_max(ms));
+    const float Ms = (Mn == -__builtin_inff()) ? 0.f : Mn;
+    const float keep = (M == -__builtin_inff()) ? 0.f : fast_exp2(M - Ms);
+    acc0 *= keep;
+    acc1 *= keep;
+    lpart *= keep;
+    const float w = (ms == -__builtin_inff()) ? 0.f : fast_exp2(ms - Ms);
+    lpart += w * ls;
 #pragma unroll
-        for (int j = 0; j < C; ++j) {
-          const float* os = orow_of(s0 + min(j0 + j, n - 1));
-          v0[j] = os[dv0];
-          v1[j] = os[dv1];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < C; ++j) {
-        const float wj = __shfl(w, j0 + j);
-        if (j0 + j < n) {
-          acc0 += wj * v0[j];
-          acc1 += wj * v1[j];
-        }
-      }
+    for (int j = 0; j < C; ++j) {
+      const float wj = __shfl(w, j);   // 0 for j >= n
+      acc0 += wj * v0[j];
+      acc1 += wj * v1[j];
     }
+    M = Mn;
   }
   const float lsum = wave_sum(lpart);
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
@@ -147,8 +158,9 @@ __global__ __launch_bounds__(64) void split_merge_kernel(AttnArgs a, int DV) {
   idx /= R;
   const int hkv = idx % a.Hkv;
   const int b = idx / a.Hkv;
+  const int split_len = split_length(a, a.causal != 0);
   const SeqInfo si = seq_info(a, b, a.causal != 0);
-  const int nvalid = split_count(a, si);
+  const int nvalid = split_count(a, si, split_len);
   if (nvalid <= 1) return;
   merge_row<T>(a, b, hkv, r, R, nvalid, DV);
 }
@@ -179,12 +191,13 @@ __global__ __launch_bounds__(64 * NW, (DQK > 128 ? 1 : 2)) void decode_attn_kern
   // the batch of this workgroup: lanes read 64 batches' lengths at a time and
   // a wave prefix sum of their workgroup counts finds the batch that holds
   // item blockIdx.x (one memory round trip instead of one per batch)
+  const int split_len = split_length(a, CAUSAL);
   int item = blockIdx.x;
   int b = a.B;
   for (int b0 = 0; b0 < a.B; b0 += 64) {
     const int bl = b0 + lane;
     int cnt = 0;
-    if (bl < a.B) cnt = max(1, split_count(a, seq_info(a, bl, CAUSAL))) * NG;
+    if (bl < a.B) cnt = max(1, split_count(a, seq_info(a, bl, CAUSAL), split_len)) * NG;
     int incl = cnt;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -211,7 +224,7 @@ __global__ __launch_bounds__(64 * NW, (DQK > 128 ? 1 : 2)) void decode_attn_kern
   const bool row_ok = r < R;
   const int qpos = off + tok;
 
-  const int k_begin = si.kbeg + split * a.split_len;
+  const int k_begin = si.kbeg + split * split_len;
   if (k_begin >= kend_all) {
     if (kend_all == si.kbeg && split == 0 && row_ok) {
       // no keys at all: the output rows are zero and the lse is -inf
@@ -222,8 +235,8 @@ __global__ __launch_bounds__(64 * NW, (DQK > 128 ? 1 : 2)) void decode_attn_kern
     }
     return;
   }
-  const int k_end = min(kend_all, k_begin + a.split_len);
-  const int nvalid = split_count(a, si);
+  const int k_end = min(kend_all, k_begin + split_len);
+  const int nvalid = split_count(a, si, split_len);
 
   u32x4 qf[QS];   // filled once the first loads are in flight (below)
 

@@ -184,8 +184,9 @@ int attn_fwd_varlen(const attn_varlen_params* p, void* stream);
  *
  * workspace: device memory of at least attn_fwd_kvcache_workspace_size(p)
  * bytes, 256-byte aligned (NULL allowed when that size is 0); its content on
- * entry is irrelevant.  num_splits: 0 picks the split count of the
- * single-token decode path automatically; a positive value forces it.
+ * entry is irrelevant.  Calls that may overlap in time must not share a
+ * workspace.  num_splits: 0 lets the single-token decode path size its splits
+ * from the device-side cache lengths; a positive value forces the count.
  *
  * On the single-token decode path (at most 16 query rows per kv head) the
  * rotary embedding (when rotary_dim is a multiple of 16 and the tables are
@@ -223,9 +224,9 @@ int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream);
  * address is looked up once per device on the first call there.  A call
  * whose attn_fwd_kvcache_workspace_size() exceeds 16 MiB returns
  * ATTN_E_WORKSPACE before anything is enqueued (the single-token decode of
- * B=8, Hkv=8, a 8192-row cache needs 2.1 MiB).  The call allocates nothing:
- * no hipMalloc/hipFree, no host allocation.  Nothing in the array has to
- * start at zero: every byte a call reads was written earlier in that call.
+ * B=8, Hq=32, Hkv=8, a 8192-row cache needs 5.5 MiB).  The call allocates
+ * nothing: no hipMalloc/hipFree, no host allocation.  Nothing in the array has
+ * to start at zero: every byte a call reads was written earlier in that call.
  * Every call on one GPU shares its array, so calls that may overlap on one
  * GPU (different streams, or host threads without ordering between them)
  * race: order them on one stream.

@@ -246,8 +246,11 @@ def test_kvcache_workspace_plan():
     # rotation happens inside the decode kernel (rd % 16 == 0)
     p, keep = _kv(B=8, Hq=32, Hkv=8, D=128, cap=8192, rotary=128)
     need = E.kvcache_workspace_size(p)
-    split = 8192 * 8 * 8 // 2048          # about 2048 (kv head, split) waves when every cache is full
-    nsp = 8192 // split
+    # the kernels size the splits from the device-side lengths for about 1408
+    # (kv head, split) waves; the workspace holds splits down to half the
+    # length full caches would get: ceil(8192*8*8 / 2816) = 187 -> 192 keys
+    split = 192
+    nsp = (8192 + split - 1) // split
     R = 4
     cnt = 0
     assert need == cnt + _al(8 * 8 * nsp * R * 128 * 4) + _al(8 * 8 * nsp * R * 2 * 4)

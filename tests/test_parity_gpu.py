@@ -458,6 +458,17 @@ def test_kvcache_decode_window(window, causal):
     _kv_check(case, window=window, num_splits=3)
 
 
+@pytest.mark.parametrize("sq", [150, 64])
+def test_kvcache_chunk_d64_longest_first_pairs(sq):
+    # head size 64 with per-batch lengths: each workgroup takes the (batch,
+    # query tile) group of its rank in key-tile order and then the group of the
+    # mirrored rank; 3 batches of ceil(sq/64) tiles give an odd group count at
+    # sq=150 (the middle group runs alone) and an even one at sq=64
+    case = W.random_kvcache(3, sq, 8, 2, 64, 64, 1024, "fp16", snew=sq, seqlens=[0, 700, 333],
+                            rotary_dim=64, interleaved=False, causal=True, seed=53 + sq)
+    _kv_check(case)
+
+
 @pytest.mark.parametrize("window", [(30, 0), (10, 10), (-1, 2)])
 def test_kvcache_chunk_window(window):
     case = W.random_kvcache(2, 90, 4, 2, 128, 128, 512, "bf16", snew=90, seqlens=[0, 250],
