@@ -315,12 +315,24 @@ def test_kvcache_decode_two_tokens_full_rows(causal):
 
 
 def test_kvcache_decode_many_splits():
-    # capacity 131072 with one kv head per batch: the plan makes 256-key
-    # splits, so the merge combines up to 512 splits per row (several passes
-    # of 64); the second batch is half full
+    # capacity 131072 with one kv head per batch: the kernels size the splits
+    # from the two lengths (160 keys), so the merge combines about 820 splits
+    # per row of the first batch, 32 per memory round trip; the second batch
+    # is half full
     case = W.random_kvcache(2, 1, 8, 1, 128, 128, 131072, "bf16", snew=1, seqlens=[131071, 70000],
                             rotary_dim=128, seed=73)
     _kv_check(case)
+
+
+def test_kvcache_decode_more_than_64_batches():
+    # 70 batches: the split sizing and the workgroup-to-batch search read the
+    # lengths 64 at a time; empty, one-key and full caches mixed
+    g = torch.Generator().manual_seed(91)
+    lens = torch.randint(0, 255, (70,), generator=g).tolist()
+    lens[0], lens[5], lens[69] = 0, 255, 1
+    case = W.random_kvcache(70, 1, 8, 2, 64, 64, 256, "fp16", snew=1, seqlens=lens, rotary_dim=64, seed=92)
+    _kv_check(case)
+    _kv_check(case, num_splits=3)
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
