@@ -213,7 +213,10 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
   const int Sqb = ug.Sqb, qst = ug.qst, kst = ug.kst, L = ug.L, off = ug.off;
   for (int slot = 0; slot < nslots; ++slot) {
   int qt = pu;
-  if (CAUSAL && !a.lpt) qt = (PAIR && slot == 1) ? pu : nqt - 1 - pu;   // heavy tiles first
+  // heavy tiles first; a pair at head size 64 takes its light tile first
+  // (measured: workload 2 causal 20.9 -> 20.4 us; at 192/128 the light-first
+  // order is 4 % slower)
+  if (CAUSAL && !a.lpt) qt = PAIR ? ((slot == 0) == (DQK <= 64) ? pu : nqt - 1 - pu) : nqt - 1 - pu;
   // key j is allowed for the query at position p iff p - wlft <= j <= p + wrgt
   // (causal caps wrgt at 0; without a window the bounds are compile-time
   // constants and the unbounded sides drop out)
