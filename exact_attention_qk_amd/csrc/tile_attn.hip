@@ -429,6 +429,15 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
     const uint16_t* kt = lds16 + (g * 2 + s) * STAGE;
     const uint16_t* vt = kt + KT;
 
+    // Wave priorities at head size >= 128 with one key group (the two waves
+    // of a SIMD then come from different workgroups and drift freely): at
+    // 192/128 the MFMA phases run at priority 2, at 128 the softmax at 3
+    // (measured on four boxes: 192/128 S=4096 causal -2..-3 %, 128 S=4096
+    // causal -3.5..-5 %; no gain or a loss at head size 64 and with two key
+    // groups, so those stay at the default)
+    constexpr bool PRIO = DQK >= 128 && NS == 1 && !F8;
+    constexpr int PRIO_MFMA = DQK >= 192 ? 2 : 0, PRIO_SOFT = DQK >= 192 ? 0 : 3;
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(PRIO_MFMA);
     // ---- S^T = K Q^T for two 32-key blocks
     f32x16 sc[RB][NKB];
     bool blk_on[NKB];
@@ -506,6 +515,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
       }
     }
 
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(PRIO_SOFT);
     // ---- mask, row max, lazy rescale, P
     const bool need_mask = (key0 + BN > L) || ((WIN || CAUSAL) && key0 + BN - 1 > pmin + wrgt) ||
                            (WIN && key0 < pmax - wlft) || (WIN && !blk_on[0]) || !blk_on[NKB - 1];
@@ -569,6 +579,7 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
       l_run[rb] = lsum;
     }
 
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(PRIO_MFMA);
     // ---- O^T += V^T P^T
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
