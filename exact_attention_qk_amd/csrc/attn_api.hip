@@ -110,6 +110,7 @@ struct KVPlan {
   bool rotq = false;        // tiled kernel rotates q as it loads it (the append pass then skips q)
   int split_len = 0, num_splits = 0;
   int split_auto = 0;       // > 0: the kernels size the splits from the device-side lengths
+  int split_slots = 0;      // splits of all batches together that the workspace holds
   size_t off_qrot = 0, off_o = 0, off_ml = 0, total = 0;
 };
 
@@ -144,18 +145,23 @@ KVPlan plan_kvcache(const attn_kvcache_params* p) {
       // about kSplitWaves (kv head, split) waves in all (a workgroup holds the
       // waves of up to 8 kv heads of one split, so about 176 workgroups on the
       // 256-CU MI355X; measured on random cache fills, more splits cost more
-      // in the merge than they gain).  The workspace holds splits down to
-      // half the length that full caches would get.
+      // in the merge than they gain), and never below one 32-key step.
       k.split_auto = kSplitWaves;
-      const double per = (double)cap * p->B * p->Hkv / (2.0 * kSplitWaves);
-      len = (int)std::ceil(per);
-      if (len > 2048) len = 2048;
+      len = 32;
     }
     len = (len + 31) / 32 * 32;
     if (len < 32) len = 32;
     k.split_len = len;
     k.num_splits = (cap + len - 1) / len;
-    const size_t slots = (size_t)p->B * p->Hkv * k.num_splits * R;
+    // Splits are numbered across batches (a batch without keys counts one).
+    // Sized from the key counts, batch b has ceil(n_b / len) < n_b / len + 1
+    // splits with len >= total * Hkv / kSplitWaves, so all batches together
+    // have fewer than kSplitWaves / Hkv + B; whatever the lengths, the cache
+    // capacity bounds each batch to num_splits.
+    int64_t slots_all = (int64_t)p->B * k.num_splits;
+    if (k.split_auto) slots_all = std::min<int64_t>(slots_all, kSplitWaves / p->Hkv + p->B + 1);
+    k.split_slots = (int)slots_all;
+    const size_t slots = (size_t)k.split_slots * p->Hkv * R;
     k.off_o = off;
     off = align_up(off + slots * p->Dv * sizeof(float));
     k.off_ml = off;
@@ -654,6 +660,7 @@ int run_kvcache(const attn_kvcache_params* p, hipStream_t st, char* ws) {
     a.ws_o = reinterpret_cast<float*>(ws + plan.off_o);
     a.ws_ml = reinterpret_cast<float*>(ws + plan.off_ml);
     a.split_auto = plan.split_auto;
+    a.split_slots = plan.split_slots;
     if (plan.fused) {
       a.fused = 1;
       if (p->Snew > 0) {

@@ -32,8 +32,9 @@ struct AttnArgs {
   // split-KV decode
   int split_len, num_splits;   // split length (the smallest one when split_auto), splits per batch at most
   int split_auto;             // 0, or the number of (kv head, split) waves the kernels size splits for
-  float* ws_o;                // [B, Hkv, num_splits, R, Dv] fp32 partial numerators
-  float* ws_ml;               // [B, Hkv, num_splits, R, 2]  running max (log2 units), sum
+  int split_slots;            // splits of all batches together that the workspace holds
+  float* ws_o;                // [split_slots, Hkv, R, Dv] fp32 partial numerators, a batch's splits adjacent
+  float* ws_ml;               // [split_slots, Hkv, R, 2]  running max (log2 units), sum
   // decode with the append and the rotary embedding done in the same kernel
   int fused;                  // 1: keys >= c_b come from kn/vn (rotated) and are written to the cache
   const uint16_t* kn; int64_t kn_sb, kn_ss, kn_sh;

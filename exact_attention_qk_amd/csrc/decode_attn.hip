@@ -73,9 +73,10 @@ __device__ __forceinline__ int split_count(const AttnArgs& a, const SeqInfo& s, 
 }
 
 // Split length: fixed by the host (split_auto == 0), or sized from the
-// actual key counts so that all batches together make about split_auto
-// (kv head, split) waves, never shorter than a.split_len (the length the
-// workspace was sized for).  Every lane of a wave returns the same value.
+// actual key counts so that all batches together make at most split_auto
+// (kv head, split) waves plus one split per batch (the bound the workspace
+// and the grid are sized for), never shorter than a.split_len (one 32-key
+// step).  Every lane of a wave returns the same value.
 __device__ __forceinline__ int split_length(const AttnArgs& a, bool causal) {
   if (!a.split_auto) return a.split_len;
   const int lane = threadIdx.x & 63;
@@ -95,31 +96,53 @@ __device__ __forceinline__ int split_length(const AttnArgs& a, bool causal) {
   return max(a.split_len, (int)((want + 31) / 32 * 32));
 }
 
-// Combine the nvalid splits of query row r of (b, hkv) (one wave).  A lane
-// owns output columns lane and lane + 64.  Splits are taken 32 at a time: the
-// partial outputs of the chunk and, on lane j, the maximum and sum of its
-// split j are requested together, so a chunk costs one round trip to memory;
-// chunks are combined with a running maximum, and split weights are
-// broadcast with cross-lane reads.
+// Splits are numbered across batches in batch order (a batch without keys
+// counts one, as the attention kernel gives it one workgroup); the partials
+// of split s, kv head h, query row r sit at slot (s * Hkv + h) * R + r.  The
+// index of batch b's first split, from a lane-parallel count over the batches
+// before it.
+__device__ __forceinline__ int first_split(const AttnArgs& a, int b, bool causal, int split_len) {
+  const int lane = threadIdx.x & 63;
+  int before = 0;
+  for (int b0 = 0; b0 < b; b0 += 64) {
+    const int bl = b0 + lane;
+    int n = bl < b ? max(1, split_count(a, seq_info(a, bl, causal), split_len)) : 0;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) n += __shfl_xor(n, m);
+    before += n;
+  }
+  return before;
+}
+
+// Combine the splits of query row r of (b, hkv) (one wave).  A lane owns
+// output columns lane and lane + 64.  Splits are taken 32 at a time: the
+// partial outputs of a chunk and, on lane j, the maximum and sum of its split
+// j are requested together, so a chunk costs one round trip to memory.
+// Chunks are combined with a running maximum, and split weights are broadcast
+// with cross-lane reads.
 template <class T>
-__device__ void merge_row(const AttnArgs& a, int b, int hkv, int r, int R, int nvalid, int DV) {
+__device__ void merge_row(const AttnArgs& a, int b, int hkv, int r, int R, int DV, bool causal) {
   constexpr int C = 32;
   const int lane = threadIdx.x;
   const int dv0 = min(lane, DV - 1), dv1 = min(lane + 64, DV - 1);   // clamped: loads never branch
   const int tok = r / a.group;
   const int hq = hkv * a.group + (r - tok * a.group);
-  const int64_t slot0 = ((int64_t)b * a.Hkv + hkv) * a.num_splits * R + r;
+  const int split_len = split_length(a, causal);
+  const int nvalid = split_count(a, seq_info(a, b, causal), split_len);
+  if (nvalid <= 1) return;   // finished by the attention kernel
+  const int64_t stride = (int64_t)a.Hkv * R;   // between consecutive splits
+  const int64_t slot0 = (int64_t)first_split(a, b, causal, split_len) * stride + (int64_t)hkv * R + r;
   float M = -__builtin_inff(), lpart = 0.f, acc0 = 0.f, acc1 = 0.f;
   for (int s0 = 0; s0 < nvalid; s0 += C) {
     const int n = min(C, nvalid - s0);
     float v0[C], v1[C];
 #pragma unroll
     for (int j = 0; j < C; ++j) {
-      const float* os = a.ws_o + (slot0 + (int64_t)(s0 + min(j, n - 1)) * R) * DV;
+      const float* os = a.ws_o + (slot0 + (int64_t)(s0 + min(j, n - 1)) * stride) * DV;
       v0[j] = os[dv0];
       v1[j] = os[dv1];
     }
-    const float* ml = a.ws_ml + (slot0 + (int64_t)(s0 + min(lane, n - 1)) * R) * 2;
+    const float* ml = a.ws_ml + (slot0 + (int64_t)(s0 + min(lane, n - 1)) * stride) * 2;
     const float ms = lane < n ? ml[0] : -__builtin_inff();
     const float ls = lane < n ? ml[1] : 0.f;
     const float Mn = fmaxf(M, wave_max(ms));
@@ -158,11 +181,7 @@ __global__ __launch_bounds__(64) void split_merge_kernel(AttnArgs a, int DV) {
   idx /= R;
   const int hkv = idx % a.Hkv;
   const int b = idx / a.Hkv;
-  const int split_len = split_length(a, a.causal != 0);
-  const SeqInfo si = seq_info(a, b, a.causal != 0);
-  const int nvalid = split_count(a, si, split_len);
-  if (nvalid <= 1) return;
-  merge_row<T>(a, b, hkv, r, R, nvalid, DV);
+  merge_row<T>(a, b, hkv, r, R, DV, a.causal != 0);
 }
 
 template <class T, int DQK, int DV, bool CAUSAL, bool FUSED, int NW>
@@ -415,7 +434,9 @@ __global__ __launch_bounds__(64 * NW, (DQK > 128 ? 1 : 2)) void decode_attn_kern
     return;
   }
   if (row_ok) {
-    const int64_t slot = (((int64_t)b * a.Hkv + hkv) * a.num_splits + split) * R + r;
+    // this workgroup's split among all batches' splits: workgroups are
+    // numbered (split, kv-head group) in batch order
+    const int64_t slot = ((int64_t)(blockIdx.x / NG) * a.Hkv + hkv) * R + r;
     float* wo = a.ws_o + slot * DV;
 #pragma unroll
     for (int i = 0; i < DVB; ++i)
@@ -430,7 +451,7 @@ __global__ __launch_bounds__(64 * NW, (DQK > 128 ? 1 : 2)) void decode_attn_kern
 // ---------------------------------------------------------------- launchers
 template <class T, int DQK, int DV, int NW>
 static hipError_t launch_decode_nw(const AttnArgs& a, bool causal, hipStream_t st) {
-  const dim3 grid((unsigned)((a.Hkv / NW) * a.num_splits * a.B)), block(64 * NW);
+  const dim3 grid((unsigned)((a.Hkv / NW) * a.split_slots)), block(64 * NW);
   if (a.fused) {
     if (causal)
       hipLaunchKernelGGL((decode_attn_kernel<T, DQK, DV, true, true, NW>), grid, block, 0, st, a);

@@ -186,7 +186,9 @@ int attn_fwd_varlen(const attn_varlen_params* p, void* stream);
  * bytes, 256-byte aligned (NULL allowed when that size is 0); its content on
  * entry is irrelevant.  Calls that may overlap in time must not share a
  * workspace.  num_splits: 0 lets the single-token decode path size its splits
- * from the device-side cache lengths; a positive value forces the count.
+ * from the device-side cache lengths (at least 32 keys each, about 1408
+ * (kv head, split) pairs in all, so its workspace does not grow with the
+ * capacity); a positive value forces the count per batch.
  *
  * On the single-token decode path (at most 16 query rows per kv head) the
  * rotary embedding (when rotary_dim is a multiple of 16 and the tables are
@@ -224,7 +226,8 @@ int attn_fwd_kvcache(const attn_kvcache_params* p, void* stream);
  * address is looked up once per device on the first call there.  A call
  * whose attn_fwd_kvcache_workspace_size() exceeds 16 MiB returns
  * ATTN_E_WORKSPACE before anything is enqueued (the single-token decode of
- * B=8, Hq=32, Hkv=8, a 8192-row cache needs 5.5 MiB).  The call allocates
+ * B=8, Hq=32, Hkv=8, D=128 with automatic splits needs 2.9 MiB whatever the
+ * capacity).  The call allocates
  * nothing: no hipMalloc/hipFree, no host allocation.  Nothing in the array has
  * to start at zero: every byte a call reads was written earlier in that call.
  * Every call on one GPU shares its array, so calls that may overlap on one

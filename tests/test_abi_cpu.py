@@ -242,18 +242,21 @@ def _al(x):
 
 
 def test_kvcache_workspace_plan():
-    # decode path: partials for every (batch, kv head, split, row); the
-    # rotation happens inside the decode kernel (rd % 16 == 0)
+    # decode path: partials for every (split, kv head, row), splits numbered
+    # across batches; the rotation happens inside the decode kernel
+    # (rd % 16 == 0).  The kernels size the splits from the device-side
+    # lengths for at most 1408 (kv head, split) waves plus one split per
+    # batch: 1408 // 8 + 8 + 1 = 185 splits (a 8192-row cache alone would
+    # allow 8 * 256 splits of 32 keys)
     p, keep = _kv(B=8, Hq=32, Hkv=8, D=128, cap=8192, rotary=128)
     need = E.kvcache_workspace_size(p)
-    # the kernels size the splits from the device-side lengths for about 1408
-    # (kv head, split) waves; the workspace holds splits down to half the
-    # length full caches would get: ceil(8192*8*8 / 2816) = 187 -> 192 keys
-    split = 192
-    nsp = (8192 + split - 1) // split
+    nsp = 1408 // 8 + 8 + 1
     R = 4
     cnt = 0
-    assert need == cnt + _al(8 * 8 * nsp * R * 128 * 4) + _al(8 * 8 * nsp * R * 2 * 4)
+    assert need == cnt + _al(nsp * 8 * R * 128 * 4) + _al(nsp * 8 * R * 2 * 4)
+    # a short capacity bounds the splits instead: 8 batches x 2 splits of 32
+    p2, keep2 = _kv(B=8, Hq=32, Hkv=8, D=128, cap=64, rotary=128)
+    assert E.kvcache_workspace_size(p2) == _al(16 * 8 * R * 128 * 4) + _al(16 * 8 * R * 2 * 4)
     # forcing one split
     p.num_splits = 1
     assert E.kvcache_workspace_size(p) == cnt + _al(8 * 8 * 1 * R * 128 * 4) + _al(8 * 8 * R * 2 * 4)
@@ -261,8 +264,8 @@ def test_kvcache_workspace_plan():
     # pass, whose rotated q copy comes first
     p, keep = _kv(B=8, Hq=32, Hkv=8, D=128, cap=8192, rotary=40)
     q_rot = 8 * 1 * 32 * 128 * 2
-    assert E.kvcache_workspace_size(p) == cnt + _al(q_rot) + _al(8 * 8 * nsp * R * 128 * 4) + \
-        _al(8 * 8 * nsp * R * 2 * 4)
+    assert E.kvcache_workspace_size(p) == cnt + _al(q_rot) + _al(nsp * 8 * R * 128 * 4) + \
+        _al(nsp * 8 * R * 2 * 4)
     # chunked prefill (many query rows): q is rotated as the tiled kernel loads
     # it when the rotary width is a multiple of 16; otherwise a rotated copy
     p, keep = _kv(B=4, Sq=512, Hq=16, Hkv=16, D=128, cap=4096, snew=512, rotary=64)

@@ -212,7 +212,7 @@ def test_workload_fwd_asym_full():
 
 # ---------------------------------------------------------------- kvcache
 
-def _kv_run(case, num_splits=0, return_lse=True, share_q=False, window=(-1, -1)):
+def _kv_run(case, num_splits=0, return_lse=True, share_q=False, window=(-1, -1), workspace=None):
     """Run the HIP kvcache path on device copies; returns (out, lse, k_cache, v_cache)."""
     q = dev(case.q)
     if share_q:
@@ -225,7 +225,8 @@ def _kv_run(case, num_splits=0, return_lse=True, share_q=False, window=(-1, -1))
                                     rotary_sin=dev(case.rotary_sin), cache_seqlens=cs,
                                     causal=case.causal, softmax_scale=case.softmax_scale,
                                     rotary_interleaved=case.rotary_interleaved,
-                                    num_splits=num_splits, return_lse=True, window_size=window)
+                                    num_splits=num_splits, return_lse=True, window_size=window,
+                                    workspace=workspace)
     torch.cuda.synchronize()
     return out, lse, kc, vc
 
@@ -257,8 +258,8 @@ def _bits_equal(gpu_cache, ref_cache, dtype):
     return bool(same.all())
 
 
-def _kv_check(case, num_splits=0, share_q=False, window=(-1, -1)):
-    out, lse, kc, vc = _kv_run(case, num_splits, share_q=share_q, window=window)
+def _kv_check(case, num_splits=0, share_q=False, window=(-1, -1), workspace=None):
+    out, lse, kc, vc = _kv_run(case, num_splits, share_q=share_q, window=window, workspace=workspace)
     ref, rlse, rkc, rvc = _kv_oracle(case, window)
     err = maxabs(out, ref)
     assert err <= TOL[case.dtype], "max abs err %.3e" % err
@@ -333,6 +334,17 @@ def test_kvcache_decode_more_than_64_batches():
     case = W.random_kvcache(70, 1, 8, 2, 64, 64, 256, "fp16", snew=1, seqlens=lens, rotary_dim=64, seed=92)
     _kv_check(case)
     _kv_check(case, num_splits=3)
+
+
+@pytest.mark.parametrize("num_splits", [0, 9])
+def test_kvcache_merge_ignores_stale_workspace(num_splits):
+    # the merge requests its first 32 splits before it knows how many a row
+    # has; a workspace full of NaN bits (left by nothing this call writes)
+    # must not leak into rows with fewer splits: lengths from 0 to 3000
+    case = W.random_kvcache(4, 1, 8, 2, 128, 128, 4096, "bf16", snew=1, seqlens=[3000, 40, 0, 700],
+                            rotary_dim=64, seed=95)
+    ws = torch.full((64 << 20,), 0xFF, dtype=torch.uint8, device="cuda")
+    _kv_check(case, num_splits=num_splits, workspace=ws)
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
