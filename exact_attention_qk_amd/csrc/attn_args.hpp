@@ -27,6 +27,7 @@ struct AttnArgs {
   int num_qtiles;             // tiled kernel: ceil(Sq / rows per workgroup)
   int xcd_remap;              // tiled kernel: 1 when the grid is a multiple of 8
   int lpt;                    // tiled kernel: longest-first unit order from the device-side lengths
+  int qmajor;                 // tiled kernel, causal: units ordered by query tile, last (heaviest) first
   float c;                    // softmax_scale * log2(e)
   float oscale;               // FP8 inputs: the descale of v, applied to the output
   // split-KV decode

@@ -52,10 +52,13 @@ __device__ __forceinline__ float wave_sum(float x) {
 struct SeqInfo {
   int L, off, kbeg, kend, wl, wr;   // key length, position of query token 0, key range, window
 };
-__device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b, bool causal) {
+// cache length c_b of batch b (0 outside the KV-cache mode, where it is unused)
+__device__ __forceinline__ int cache_len(const AttnArgs& a, int b) {
+  return a.kvcache ? (a.seqlens ? a.seqlens[b] : a.seqlen_scalar) : 0;
+}
+__device__ __forceinline__ SeqInfo seq_from(const AttnArgs& a, int cb, bool causal) {
   SeqInfo s;
   if (a.kvcache) {
-    const int cb = a.seqlens ? a.seqlens[b] : a.seqlen_scalar;
     s.L = cb + a.Snew;
     s.off = cb;
   } else {
@@ -68,6 +71,9 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b, bool causa
   s.kbeg = min(s.kend, max(0, s.off - s.wl));
   return s;
 }
+__device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b, bool causal) {
+  return seq_from(a, cache_len(a, b), causal);
+}
 __device__ __forceinline__ int split_count(const AttnArgs& a, const SeqInfo& s, int split_len) {
   return min(a.num_splits, (s.kend - s.kbeg + split_len - 1) / split_len);
 }
@@ -77,6 +83,16 @@ __device__ __forceinline__ int split_count(const AttnArgs& a, const SeqInfo& s, 
 // (kv head, split) waves plus one split per batch (the bound the workspace
 // and the grid are sized for), never shorter than a.split_len (one 32-key
 // step).  Every lane of a wave returns the same value.
+__device__ __forceinline__ int split_length_of(const AttnArgs& a, int tot) {
+  if (!a.split_auto) return a.split_len;
+  const int64_t want = ((int64_t)tot * a.Hkv + a.split_auto - 1) / a.split_auto;
+  return max(a.split_len, (int)((want + 31) / 32 * 32));
+}
+__device__ __forceinline__ int wave_isum(int n) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) n += __shfl_xor(n, m);
+  return n;
+}
 __device__ __forceinline__ int split_length(const AttnArgs& a, bool causal) {
   if (!a.split_auto) return a.split_len;
   const int lane = threadIdx.x & 63;
@@ -127,11 +143,27 @@ __device__ void merge_row(const AttnArgs& a, int b, int hkv, int r, int R, int D
   const int dv0 = min(lane, DV - 1), dv1 = min(lane + 64, DV - 1);   // clamped: loads never branch
   const int tok = r / a.group;
   const int hq = hkv * a.group + (r - tok * a.group);
-  const int split_len = split_length(a, causal);
-  const int nvalid = split_count(a, seq_info(a, b, causal), split_len);
+  int nvalid, first;
+  if (a.B <= 64) {
+    // one load of every batch's length gives the split length, this batch's
+    // split count and the index of its first split
+    int n = 0;
+    if (lane < a.B) {
+      const SeqInfo sl = seq_from(a, cache_len(a, lane), causal);
+      n = sl.kend - sl.kbeg;
+    }
+    const int split_len = split_length_of(a, wave_isum(n));
+    const int cnt = lane < a.B ? min(a.num_splits, (n + split_len - 1) / split_len) : 0;
+    nvalid = __shfl(cnt, b);
+    first = wave_isum(lane < b ? max(1, cnt) : 0);
+  } else {
+    const int split_len = split_length(a, causal);
+    nvalid = split_count(a, seq_info(a, b, causal), split_len);
+    first = nvalid <= 1 ? 0 : first_split(a, b, causal, split_len);
+  }
   if (nvalid <= 1) return;   // finished by the attention kernel
   const int64_t stride = (int64_t)a.Hkv * R;   // between consecutive splits
-  const int64_t slot0 = (int64_t)first_split(a, b, causal, split_len) * stride + (int64_t)hkv * R + r;
+  const int64_t slot0 = (int64_t)first * stride + (int64_t)hkv * R + r;
   float M = -__builtin_inff(), lpart = 0.f, acc0 = 0.f, acc1 = 0.f;
   for (int s0 = 0; s0 < nvalid; s0 += C) {
     const int n = min(C, nvalid - s0);
@@ -209,32 +241,57 @@ __global__ __launch_bounds__(64 * NW, (DQK > 128 ? 1 : 2)) void decode_attn_kern
   const int NG = a.Hkv / NW;
   // the batch of this workgroup: lanes read 64 batches' lengths at a time and
   // a wave prefix sum of their workgroup counts finds the batch that holds
-  // item blockIdx.x (one memory round trip instead of one per batch)
-  const int split_len = split_length(a, CAUSAL);
-  int item = blockIdx.x;
-  int b = a.B;
-  for (int b0 = 0; b0 < a.B; b0 += 64) {
-    const int bl = b0 + lane;
-    int cnt = 0;
-    if (bl < a.B) cnt = max(1, split_count(a, seq_info(a, bl, CAUSAL), split_len)) * NG;
+  // item blockIdx.x (one memory round trip per 64 batches)
+  int split_len, item = blockIdx.x, b = a.B, cb = 0;
+  if (a.B <= 64) {
+    // one load of every batch's length serves the split length, the search
+    // and the batch's own bounds (the first K/V loads wait for it alone)
+    const int cl = lane < a.B ? cache_len(a, lane) : 0;
+    int n = 0;
+    if (lane < a.B) {
+      const SeqInfo sl = seq_from(a, cl, CAUSAL);
+      n = sl.kend - sl.kbeg;
+    }
+    split_len = split_length_of(a, wave_isum(n));
+    const int cnt = lane < a.B ? max(1, min(a.num_splits, (n + split_len - 1) / split_len)) * NG : 0;
     int incl = cnt;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const int t = __shfl_up(incl, d);
       if (lane >= d) incl += t;
     }
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(bl < a.B && item < incl);
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < a.B && item < incl);
     if (hit) {
-      const int first = __builtin_ctzll(hit);
-      b = b0 + first;
-      item -= __shfl(incl - cnt, first);   // workgroups of earlier batches in this chunk
-      break;
+      b = __builtin_ctzll(hit);
+      item -= __shfl(incl - cnt, b);
+      cb = __shfl(cl, b);
     }
-    item -= __shfl(incl, 63);
+  } else {
+    split_len = split_length(a, CAUSAL);
+    for (int b0 = 0; b0 < a.B; b0 += 64) {
+      const int bl = b0 + lane;
+      int cnt = 0;
+      if (bl < a.B) cnt = max(1, split_count(a, seq_info(a, bl, CAUSAL), split_len)) * NG;
+      int incl = cnt;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(incl, d);
+        if (lane >= d) incl += t;
+      }
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(bl < a.B && item < incl);
+      if (hit) {
+        const int first = __builtin_ctzll(hit);
+        b = b0 + first;
+        item -= __shfl(incl - cnt, first);   // workgroups of earlier batches in this chunk
+        break;
+      }
+      item -= __shfl(incl, 63);
+    }
+    if (b < a.B) cb = cache_len(a, b);
   }
   if (b >= a.B) return;   // surplus workgroup
   const int split = item / NG, hkv = (item - split * NG) * NW + w;
-  const SeqInfo si = seq_info(a, b, CAUSAL);
+  const SeqInfo si = seq_from(a, cb, CAUSAL);
   const int L = si.L, off = si.off, kend_all = si.kend, wlft = si.wl, wrgt = si.wr;
   const int R = a.group * a.Sq;
   const int r = lane & 15, kg = lane >> 4;
