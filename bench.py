@@ -18,7 +18,8 @@ resident in HBM.  Each timed loop is preceded by 50 ms of the same calls,
 untimed (the engine clock ramps up over the first ~10 ms of load), and then
 by the requested warmup calls.  The headline, decode and chunked-prefill calls cycle through
 input replicas (2, 4 and 4) whose total exceeds the 256 MB Infinity Cache, so
-each call reads HBM rather than that cache.
+each call reads HBM rather than that cache; the workload-2 calls are timed on one
+input (their headline figure) and again over 16 replicas ("us_16_replicas").
 """
 from __future__ import annotations
 
@@ -271,9 +272,17 @@ def main():
             out = torch.empty_like(q)
             call = E.prepare_fwd(q, k, v, out, causal, c2.softmax_scale)
             t = time_loop([call], K, Wm, torch)
+            # the same call over 16 input replicas (16 x 16.8 MB > the 256 MB Infinity
+            # Cache): each call then reads q, k, v from HBM
+            reps = []
+            for r in range(16):
+                qr, kr, vr = c2.q.to(dev), c2.k.to(dev), c2.v.to(dev)
+                reps.append(E.prepare_fwd(qr, kr, vr, torch.empty_like(qr), causal, c2.softmax_scale))
+            t_rot = time_loop(reps, K, Wm, torch)
+            del reps, qr, kr, vr
             fl = W.fwd_flops(2, 2048, 2048, 8, 64, 64, causal)
             nm = "C2_fwd_b2h8s2048d64" + ("_causal" if causal else "")
-            configs[nm] = {"us": t * 1e6, "gflop": fl / 1e9, "tflops": fl / t / 1e12,
+            configs[nm] = {"us": t * 1e6, "us_16_replicas": t_rot * 1e6, "gflop": fl / 1e9, "tflops": fl / t / 1e12,
                            "pct_mfma_peak": 100 * fl / t / 1e12 / pk["mfma_bf16_tflops"],
                            "roofline": mfma_entry(nm, fl, t, pk, "tile_attn_kernel<F16,64,64,%s>"
                                                   % ("causal" if causal else "non-causal"))}
