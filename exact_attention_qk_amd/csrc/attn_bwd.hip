@@ -23,8 +23,8 @@
 //    over the group in registers needs no atomics.
 // Inside a workgroup, key-split (dQ) or row-split (dK/dV) groups of waves
 // walk disjoint tiles and add their partial sums through LDS at the end;
-// causal units pair complementary tiles so that every workgroup does about
-// the same amount of work.
+// causal launches dispatch the longest tiles of every head first, so the
+// short ones fill the tail (a complementary-pair mode remains in the kernels).
 // Both stream through double-buffered LDS stages filled by buffer loads whose
 // resource ends at the last valid row (rows past it read as zero and are
 // masked).  Masks: key length, causal (bottom-right), local window.
@@ -584,12 +584,14 @@ static hipError_t launch_dkdv(BwdArgs a, hipStream_t st) {
 }
 
 // Shapes per head size: eight-wave workgroups (two waves per SIMD) where the
-// registers allow it, causal tiles in complementary pairs.
+// registers allow it; causal launches take the longest tiles first over all
+// heads (measured at B2 H8 S2048 D64: 68.8 -> 67.4 us against complementary
+// tile pairs).
 template <class T, int DQK, int DV, bool CAUSAL, bool WIN>
 static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   hipError_t e;
   if constexpr (DQK <= 64) {
-    if constexpr (CAUSAL) e = launch_dq<T, DQK, DV, CAUSAL, WIN, 2, 4, true, 2>(a, st);
+    if constexpr (CAUSAL) e = launch_dq<T, DQK, DV, CAUSAL, WIN, 2, 4, false, 2>(a, st);
     else e = launch_dq<T, DQK, DV, CAUSAL, WIN, 4, 2, false, 2>(a, st);
   } else if constexpr (DQK <= 128) {
     if constexpr (CAUSAL) e = launch_dq<T, DQK, DV, CAUSAL, WIN, 2, 4, false, 2>(a, st);
@@ -599,7 +601,7 @@ static hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   }
   if (e != hipSuccess) return e;
   if constexpr (DQK <= 64) {
-    if constexpr (CAUSAL) return launch_dkdv<T, DQK, DV, CAUSAL, WIN, 2, 4, true, 2>(a, st);
+    if constexpr (CAUSAL) return launch_dkdv<T, DQK, DV, CAUSAL, WIN, 2, 4, false, 2>(a, st);
     else return launch_dkdv<T, DQK, DV, CAUSAL, WIN, 4, 2, false, 2>(a, st);
   } else if constexpr (DQK <= 128) {
     return launch_dkdv<T, DQK, DV, CAUSAL, WIN, 4, 2, false, 2, true>(a, st);
