@@ -562,6 +562,16 @@ def test_varlen_grid_larger_than_needed():
     _varlen_check(case, max_seqlen_q=700)
 
 
+@pytest.mark.parametrize("dqk,dv,dtype,causal", [(64, 64, "fp16", True), (128, 128, "bf16", True),
+                                                 (64, 64, "fp16", False)])
+def test_varlen_many_groups(dqk, dv, dtype, causal):
+    # 12 sequences up to 611 rows: more than 64 (sequence, query tile) groups, so the
+    # longest-first ranking runs through LDS instead of one wave's registers
+    lens = [611, 3, 250, 0, 480, 77, 129, 600, 1, 333, 64, 500]
+    case = W.random_varlen(lens, lens, 4, 2, dqk, dv, dtype, causal, seed=47 + dqk)
+    _varlen_check(case)
+
+
 def test_varlen_equal_lengths_bitwise_batched():
     # packed sequences of one length are the batched layout: same kernel, same bits
     B, S = 3, 300
