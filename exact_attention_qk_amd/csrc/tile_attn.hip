@@ -223,8 +223,8 @@ __global__ __launch_bounds__(64 * NR * NS, MINW) void tile_attn_kernel(AttnArgs 
   for (int slot = 0; slot < nslots; ++slot) {
   int qt = pu;
   // heavy tiles first; a pair at head size 64 takes its light tile first
-  // (measured: workload 2 causal 20.9 -> 20.4 us; at 192/128 the light-first
-  // order is 4 % slower)
+  // (measured on the paired B2 H8 S2048 causal launch: 20.9 -> 20.4 us; at
+  // 192/128 the light-first order is 4 % slower)
   if (CAUSAL && !a.lpt) qt = PAIR ? ((slot == 0) == (DQK <= 64) ? pu : nqt - 1 - pu) : nqt - 1 - pu;
   // key j is allowed for the query at position p iff p - wlft <= j <= p + wrgt
   // (causal caps wrgt at 0; without a window the bounds are compile-time
@@ -757,18 +757,19 @@ static hipError_t launch_dims(const AttnArgs& a, bool fastc, hipStream_t st) {
   if constexpr (DQK <= 16) {
     return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 4, 1, 64, false, 2, F8, ROTQ>(a, fastc, st);
   } else if constexpr (DQK <= 64) {
-    // causal, no window, at most 65536 rows: complementary tile pairs (every
-    // workgroup the same work); a causal band (window) gives every tile about
-    // the same work already, and larger causal problems balance by dispatching
-    // the longest tiles first (measured: window (256, 256) 14.4 -> 11.2 us,
-    // B4 H16 S8192 causal 781 -> 700 us)
-    // packed sequences size the grid by the longest one, so pairs would mostly
-    // meet tiles past a shorter sequence's end: heavy-first order instead
-    // (7 packed sequences: 21.3 -> 19.6 us)
-    // equal lengths: 64-row units without pairing, heaviest query tiles of
-    // every head first; two workgroups fit a CU (64 KB of LDS each), so a CU
-    // runs 16 waves and the dispatcher balances the tail (measured: workload 2
-    // causal 20.1 -> 18.6 us against the complementary pairs)
+    // causal, no window, at most 65536 rows: 64-row units of 32-key tiles.
+    //  * equal lengths: no pairing, heaviest query tiles of every head first;
+    //    two workgroups fit a CU (64 KB of LDS each), so a CU runs 16 waves
+    //    and the dispatcher balances the tail (measured: B2 H8 S2048 causal
+    //    20.1 -> 18.6 us against complementary tile pairs);
+    //  * packed sequences size the grid by the longest one, so pairs would
+    //    mostly meet tiles past a shorter sequence's end: longest first from
+    //    the device-side lengths (7 packed sequences: 21.3 -> 19.6 us);
+    //  * KV caches: complementary tile pairs (every workgroup the same work).
+    // A causal band (window) gives every tile about the same work already,
+    // and larger causal problems balance by dispatching the longest tiles
+    // first (measured: window (256, 256) 14.4 -> 11.2 us, B4 H16 S8192 causal
+    // 781 -> 700 us).
     if constexpr (CAUSAL && !WIN) {
       if (rows <= 256 * 256 && a.varlen)
         return launch_cfg<T, DQK, DV, CAUSAL, WIN, 1, 2, 4, 32, false, 2, F8, ROTQ>(a, fastc, st);
